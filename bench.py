@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the segmented MXFP8 GEMM on one MI355X.
+
+One step = one whole pass of the hot path over one batch of synthetic input:
+staging of every chunk of every rank segment through the ring, the
+block-scaled GEMM over all windows (with split-K fix-up where planned) and
+the bfloat16 epilogue -- one ``mxgemm_seg_run`` call.  Inputs are quantised
+on the GPU before timing and are resident in HBM.  Before every timed step a
+512 MiB buffer is written to push A, B and C out of L2 and the MALL.
+
+Prints ONE JSON line (rank 0 / the only rank):
+  value      = 2*M*N*K / mean step time, in TFLOP/s
+  roofline   = the GEMM kernel's algorithmic FLOP per launch / its mean launch
+               duration (HIP events around each launch, on its stream),
+               against the MI355X dense FP8 MFMA peak
+  cpu_baseline = the CPU oracle on a bounded row sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MXFP8 segmented GEMM TFLOP/s and % of MI355X MX-FP8 MFMA peak"
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 / MXFP8 MFMA
+PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 512 << 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mxfp8_block_scaled_mxgemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, sha: str):
+    """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if
+    they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"mxgemm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != sha:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s: float):
+    """Time the CPU oracle (as it stands) on the first rows of C."""
+    import numpy as np
+    import oracle
+    from mxfp8_block_scaled_mxgemm_amd import inputs
+    a32, b32 = inputs.fp32_operands(w)
+    qa, sa = oracle.quantize_mxfp8(a32)
+    qb, sb = oracle.quantize_mxfp8(b32)
+    a_seg, s_seg = inputs.split_segments(qa, w.R), inputs.split_segments(sa, w.R)
+    del a32, b32, qa, sa
+    threads = oracle.num_threads()
+    rows = max(1, threads // 2)
+    t0 = time.perf_counter()
+    oracle.mxgemm_seg_rows(a_seg, s_seg, qb, sb, 0, rows)
+    dt = time.perf_counter() - t0
+    rows = int(min(w.M, max(rows, rows * target_s / max(dt, 1e-3))))
+    rows = max(threads, (rows // threads) * threads) if rows >= threads else rows
+    t0 = time.perf_counter()
+    oracle.mxgemm_seg_rows(a_seg, s_seg, qb, sb, 0, rows)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows [0, {rows}) of C = {rows}x{w.N} outputs at K={w.K} "
+                      f"(dequantise + double-precision dot + bfloat16 rounding), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="c5", help="workload c1..c5 (default c5)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--tile-cfg", type=int, default=-1)
+    ap.add_argument("--split", type=int, default=-1)
+    ap.add_argument("--window", type=int, default=-1)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the ranks of this "
+              "method are simulated as segments in one GPU's memory, and no multi-GPU path is "
+              "built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    from mxfp8_block_scaled_mxgemm_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pkg.load()                       # fails loudly if the HIP library is missing
+    w = inputs.WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    log(f"[bench] {args.config}: {w.describe()}")
+
+    a32, b32 = inputs.fp32_operands(w)
+    a_d = torch.from_numpy(a32).to(dev)
+    b_d = torch.from_numpy(b32).to(dev)
+    del a32, b32
+    a_q, a_s = pkg.quantize_segments(a_d, w.R)
+    b_q, b_s = pkg.quantize_mxfp8(b_d)
+    del a_d, b_d
+    c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    opts = None
+    if args.tile_cfg >= 0 or args.split > 0 or args.window > 0:
+        opts = pkg.options(tile_cfg=args.tile_cfg, split=args.split, chunks_per_window=args.window)
+    g = pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts)
+    plan = g.plan.as_dict()
+    log(f"[bench] plan: {plan}")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        g.run(a_q, a_s, b_q, b_s, c, stream=stream)
+
+    def flush_caches():
+        if not args.no_flush:
+            flush.fill_(1.0)
+
+    # warm-up
+    for _ in range(max(1, args.warmup)):
+        flush_caches()
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed: stream timer --------------------------------------------
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        flush_caches()
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_mean = statistics.mean(ms)
+    log(f"[bench] stream: mean {ms_mean:.4f} ms median {statistics.median(ms):.4f} "
+        f"min {min(ms):.4f} max {max(ms):.4f}")
+
+    # ---- graph timer -----------------------------------------------------
+    graph_ms = None
+    if not args.no_graph:
+        try:
+            gs = torch.cuda.Stream()
+            graph = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.stream(gs):
+                with torch.cuda.graph(graph, stream=gs):
+                    g.run(a_q, a_s, b_q, b_s, c, stream=gs)
+            torch.cuda.synchronize()
+            gms = []
+            for i in range(args.steps):
+                flush_caches()
+                s0 = torch.cuda.Event(enable_timing=True)
+                s1 = torch.cuda.Event(enable_timing=True)
+                s0.record(stream)
+                graph.replay()
+                s1.record(stream)
+                torch.cuda.synchronize()
+                gms.append(s0.elapsed_time(s1))
+            graph_ms = statistics.median(gms)
+            log(f"[bench] graph: median {graph_ms:.4f} ms")
+            del graph
+        except Exception as e:  # report, keep the stream number
+            log(f"[bench] graph timer unavailable: {e}")
+
+    # ---- per-kernel durations (HIP events around each launch) -----------
+    g.set_profiling(True)
+    nprof = max(3, min(args.steps, 10))
+    for _ in range(nprof):
+        flush_caches()
+        step()
+    kt = g.kernel_times()
+    g.set_profiling(False)
+    torch.cuda.synchronize()
+    gemm_ms_per_launch = kt["gemm_ms"] / kt["gemm_launches"]
+    stage_ms_per_launch = kt["stage_ms"] / kt["stage_launches"]
+    flops = float(w.flops)
+    flops_per_launch = flops / plan["windows"]
+    achieved = flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
+    log(f"[bench] kernels: gemm {gemm_ms_per_launch * 1e3:.2f} us/launch x{plan['windows']}, "
+        f"stage {stage_ms_per_launch * 1e3:.2f} us/launch")
+
+    sha = kernel_source_sha()
+    traffic = load_traffic(args.config, sha)
+
+    value = flops / (ms_mean * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_mean, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {w.describe()}, "
+                               f"N(0,{w.sigma:g})" + (f" with {w.outlier_frac:.0%} of entries "
+                               f"x{w.outlier_mul:g}" if w.outlier_frac else "") +
+                               f", seed {w.seed}; MXFP8 E4M3 + E8M0/32 in, bfloat16 out",
+                   "flop_per_step": w.flops,
+                   "algorithmic_bytes_per_step": w.algorithmic_bytes,
+                   "plan": {k: plan[k] for k in ("tile_m", "tile_n", "split", "chunks_per_window",
+                                                 "windows", "grid")}},
+        "pct_of_mxfp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
+        "hbm_frac_end_to_end": round(w.algorithmic_bytes / (ms_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "timer": "stream (HIP events per step, 512 MiB cache flush before each step)"
+                 if not args.no_flush else "stream (HIP events per step, warm caches)",
+        "graph_ms_per_step_median": round(graph_ms, 5) if graph_ms is not None else None,
+        "wall_s_timed_loop_incl_flush": round(wall, 4),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "mxgemm_kernel",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "traffic": traffic,
+            "gemm_us_per_launch": round(gemm_ms_per_launch * 1e3, 3),
+            "launches_per_step": plan["windows"],
+            "stage_us_per_launch": round(stage_ms_per_launch * 1e3, 3),
+        },
+        "kernel_source_sha": sha,
+    }
+    g.close()
+    del flush, a_q, a_s, b_q, b_s, c
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a row sample")
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,194 @@
+/*
+ * mxgemm_seg -- segmented MXFP8 GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI.  Only plain integers and pointers cross it; device pointers are HIP
+ * device addresses, `stream` is a hipStream_t passed as void* (NULL = the
+ * default stream).  Every entry point returns MXGEMM_OK (0) or a negative
+ * error code; mxgemm_seg_last_error() then gives a message for the calling
+ * thread.  No entry point aborts the process.
+ *
+ * The operation is the compute half of a fused all-to-all + MXFP8 matmul
+ * (cannbot-harness 0.1.5 package diff, all_to_all_matmul_impl.h: the
+ * all-to-all/matmul class and its E4M3E4M3 kernel entry; all_to_all_matmul.cpp:
+ * problem statement `m k n rankNum`, headMSize = rows per communication
+ * chunk, bufferSize = pipeline depth).  Each of R ranks holds A as R segments
+ * of [M, kPerRank]; segment r arrives from source rank r in chunks of
+ * commMSize rows into a ring of `buffer_count` staging buffers, and the GEMM
+ * consumes the chunks that have arrived:
+ *
+ *   C[m, n] = sum_{r<R} sum_{k<kPerRank} A_r[m, k] * B[n, r*kPerRank + k]
+ *
+ * with every operand MXFP8: FP8 E4M3 (OCP "FN") codes plus one E8M0 scale
+ * byte per 32 consecutive K-elements, value = e4m3(q) * 2^(scale - 127).
+ * Products accumulate in FP32 over all segments (all_to_all_matmul_impl.h,
+ * SetupParams: splitKNum = rankSize) and C is written as bfloat16 with
+ * round-to-nearest-even.  On one GPU the R ranks are simulated: all R
+ * segments live in this GPU's memory and a staging kernel stands in for the
+ * all-to-all put.
+ */
+#ifndef MXGEMM_SEG_H
+#define MXGEMM_SEG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MXGEMM_OK = 0,
+    MXGEMM_EINVAL = -1,        /* an argument breaks a documented rule      */
+    MXGEMM_ENOMEM = -2,        /* device allocation failed                  */
+    MXGEMM_EHIP = -3,          /* a HIP runtime call failed                 */
+    MXGEMM_EUNSUPPORTED = -4   /* valid, but not supported by this build or
+                                  device (not gfx950, shape limits)         */
+};
+
+typedef struct mxgemm_seg* mxgemm_seg_t;
+
+/* Plan chosen for a problem: filled by mxgemm_seg_plan (host only, no GPU)
+ * and by mxgemm_seg_get_plan for a live handle. */
+typedef struct mxgemm_seg_plan {
+    int64_t M, kPerRank, N, K, commMSize;
+    int32_t rank_size, buffer_count;
+    int32_t chunks;            /* M / commMSize                             */
+    int32_t chunks_per_window; /* W: chunks one stage/GEMM launch pair covers */
+    int32_t windows;           /* ceil(chunks / W)                          */
+    int32_t window_slots;      /* buffer_count / W ring windows             */
+    int32_t tile_cfg;          /* index into the kernel tile table          */
+    int32_t tile_m, tile_n;    /* output tile of one work-group             */
+    int32_t split;             /* S: K split over rank-segment groups       */
+    int32_t tiles_m, tiles_n;  /* tiles of a full window                    */
+    int32_t work_items;        /* tiles_m * tiles_n * S for a full window   */
+    int32_t grid;              /* persistent work-groups per GEMM launch    */
+    int32_t group_n;           /* N-tiles per zigzag group                  */
+    int32_t num_cus;
+    int64_t slot_bytes;        /* one staging buffer: R*commMSize*kPerRank  */
+    int64_t scale_slot_bytes;  /* its scales: R*commMSize*kPerRank/32       */
+    int64_t workspace_bytes;   /* FP32 split-K partials                     */
+    int64_t counter_count;     /* split-K arrival counters                  */
+} mxgemm_seg_plan_t;
+
+/* Optional knobs for mxgemm_seg_create_ex / mxgemm_seg_plan; -1 = automatic. */
+typedef struct mxgemm_seg_options {
+    int32_t tile_cfg;          /* force a tile configuration (table index)  */
+    int32_t split;             /* force S (must divide rank_size)           */
+    int32_t chunks_per_window; /* force W (must divide buffer_count)        */
+    int32_t grid;              /* cap the persistent grid                   */
+} mxgemm_seg_options_t;
+
+/*
+ * Create a handle for one problem shape.
+ *   M          rows of A and C                         (> 0)
+ *   kPerRank   K columns per rank segment              (> 0, % 128 == 0)
+ *   rank_size  R, number of (simulated) ranks          (1 .. 64)
+ *   N          columns of C, rows of B ([N][K])        (> 0)
+ *   commMSize  rows per staged chunk                   (> 0, divides M)
+ *   buffer_count  staging ring depth                   (power of two, 1..64)
+ * Rules follow all_to_all_matmul.cpp (argument parsing: positive sizes, K
+ * divisible by rankNum) and all_to_all_matmul_impl.h (MatmulProcess: the
+ * ring index is a bit mask, so the depth is a power of two; CalcMOffset /
+ * GetCurMSize: chunks have no tail, so commMSize divides M).  The MX block is
+ * 32; this build also needs kPerRank % 128 == 0 (one MFMA K-step), else
+ * MXGEMM_EUNSUPPORTED.  Allocates, on the current device, the staging ring
+ * (buffer_count * R * commMSize * kPerRank * 33/32 bytes), the split-K
+ * workspace and counters, a side stream at default priority and the ring's
+ * events; run() allocates nothing.  Errors: EINVAL, ENOMEM, EHIP,
+ * EUNSUPPORTED (device is not gfx950).  *out is set only on success.
+ */
+int mxgemm_seg_create(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
+                      int64_t N, int64_t commMSize, int32_t buffer_count);
+
+/* As mxgemm_seg_create, with optional knobs (opts may be NULL). */
+int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
+                         int64_t N, int64_t commMSize, int32_t buffer_count,
+                         const mxgemm_seg_options_t* opts);
+
+/*
+ * Enqueue one segmented GEMM on `stream`; returns once enqueued (no host
+ * synchronisation).  All pointers are device memory, 16-byte aligned, owned
+ * by the caller, and must stay valid until the work completes:
+ *   a_seg    uint8 E4M3  [R][M][kPerRank]     segment r is rank r's K range
+ *   a_scale  uint8 E8M0  [R][M][kPerRank/32]
+ *   b        uint8 E4M3  [N][K], K = R*kPerRank, K contiguous (B transposed)
+ *   b_scale  uint8 E8M0  [N][K/32]
+ *   c        bfloat16    [M][N], fully overwritten
+ * Layouts: all_to_all_comm_udma.h, PutSegmentToRank / PutScaleToRank (source
+ * offsets r*M*rowBytes + mOffset*rowBytes), all_to_all_matmul.cpp (host
+ * buffer sizes), all_to_all_matmul_impl.h (TransB = true, C offset
+ * mOffset * N).  Chunk j (rows [j*commMSize, (j+1)*commMSize) of every
+ * segment, with their scales) is copied by a staging kernel on the handle's
+ * side stream into ring slot j % buffer_count; the GEMM for a chunk starts
+ * only after its copy (ready event) and a slot is refilled only after the
+ * GEMM that read it (credit event) -- the ready/credit pairing of
+ * MatmulProcess / AllToAllProcess.  The side stream forks from and joins
+ * back into `stream`, so work before and after run() on `stream` stays
+ * ordered and the call can be captured into a HIP graph.  A handle must not
+ * be run concurrently on two streams; distinct handles may.
+ * Errors: EINVAL (NULL handle/pointer, misaligned pointer), EHIP.
+ */
+int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const void* b,
+                   const void* b_scale, void* c, void* stream);
+
+/* Wait for the handle's work and free everything create() allocated.
+ * NULL is accepted.  Errors: EHIP (resources are still released). */
+int mxgemm_seg_destroy(mxgemm_seg_t h);
+
+/* Message for the last error on the calling thread ("" if none). */
+const char* mxgemm_seg_last_error(void);
+
+/* Copy the live handle's plan. */
+int mxgemm_seg_get_plan(mxgemm_seg_t h, mxgemm_seg_plan_t* out);
+
+/* Compute the plan create() would choose on a device with `num_cus` compute
+ * units, without touching a GPU (same rules and errors as create; opts may
+ * be NULL). */
+int mxgemm_seg_plan(mxgemm_seg_plan_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
+                    int64_t N, int64_t commMSize, int32_t buffer_count, int32_t num_cus,
+                    const mxgemm_seg_options_t* opts);
+
+/* Decode persistent work item `w` of a window with `rows` rows under `plan`
+ * into (tile row, tile column, K-split index), exactly as the GEMM kernel
+ * does (flattened work ID with zigzag N-groups; Triton-distributed-Ascend
+ * performance guide, section 1.2 on flattening the work ID and section 1.4
+ * on the zigzag swizzle).  Also returns the logical work ID the kernel's
+ * work-group `block` starts from (XCD-aware remap).  Host only.
+ * Errors: EINVAL (w or block out of range). */
+int mxgemm_seg_decode(const mxgemm_seg_plan_t* plan, int64_t rows, int32_t w, int32_t block,
+                      int32_t* tile_m_idx, int32_t* tile_n_idx, int32_t* split_idx,
+                      int32_t* first_work);
+
+/*
+ * MXFP8 quantiser: x is float32 device memory [rows][cols] with row stride
+ * ld_x elements (cols % 32 == 0); writes codes q [rows][cols] (row stride
+ * ld_q bytes) and scale bytes s [rows][cols/32] (row stride ld_s bytes).
+ * Per block of 32 consecutive elements of a row: e = the smallest integer
+ * with 448 * 2^e >= amax, clamped to [-127, 127] (amax = 0 gives -127),
+ * s = e + 127, q = E4M3 round-to-nearest-even of x * 2^-e (sign of zero
+ * kept).  The pages produce their MXFP8 inputs offline with a generator they
+ * do not show (all_to_all_matmul.cpp header: gen_data.py); this is the rule
+ * 2^ceil(log2(amax/448)) written out exactly.  Asynchronous on `stream`.
+ * Errors: EINVAL, EHIP.
+ */
+int mxgemm_quantize_mxfp8(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                          uint8_t* q, int64_t ld_q, uint8_t* s, int64_t ld_s, void* stream);
+
+/*
+ * Kernel timing for measurement.  While enabled, run() brackets every GEMM
+ * launch (on `stream`) and every staging launch (on the side stream) with
+ * timing events.  mxgemm_seg_kernel_times synchronises the handle and
+ * returns the summed durations (ms) and launch counts since the last call,
+ * then resets them.  Not for use under graph capture.  Errors: EINVAL, EHIP.
+ */
+int mxgemm_seg_set_profiling(mxgemm_seg_t h, int32_t enable);
+int mxgemm_seg_kernel_times(mxgemm_seg_t h, double* gemm_ms, int32_t* gemm_launches,
+                            double* stage_ms, int32_t* stage_launches);
+
+/* Library version string. */
+const char* mxgemm_seg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXGEMM_SEG_H */

@@ -1,0 +1,59 @@
+// Internal interface between the host library and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxg {
+
+// One row of the GEMM tile table.
+struct TileCfg {
+    int tile_m, tile_n;     // output tile of one work-group
+    int threads;            // work-group size (64-wide waves)
+    int lds_bytes;          // LDS per work-group
+    int blocks_per_cu;      // resident work-groups per compute unit
+    float rel_rate;         // planner's relative MFMA efficiency estimate
+};
+
+int num_tile_cfgs();
+const TileCfg& tile_cfg(int i);
+
+// Staging copy for one window: chunks [chunk0, chunk0 + nch) of every
+// segment, data and scales, into ring slots chunk % nbuf.
+struct StageArgs {
+    const uint8_t* a_seg;     // [R][M][kpr]
+    const uint8_t* sa_seg;    // [R][M][kpr/32]
+    uint8_t* ring;            // [nbuf][R][cms][kpr]
+    uint8_t* sring;           // [nbuf][R][cms][kpr/32]
+    int64_t M, kpr, cms;
+    int64_t slot_bytes, scale_slot_bytes;
+    int R, chunk0, nch, nbuf;
+};
+
+// GEMM over one window of `rows` staged rows.
+struct GemmArgs {
+    const uint8_t* a;         // ring data of the window's first slot
+    const uint8_t* as;        // ring scales of the window's first slot
+    int64_t a_slot_stride;    // bytes between consecutive slots (data)
+    int64_t as_slot_stride;   // bytes between consecutive slots (scales)
+    const uint8_t* b;         // [N][K]
+    const uint8_t* bs;        // [N][K/32]
+    uint16_t* c;              // C + first window row * N
+    float* ws;                // split-K partials
+    int* counters;            // split-K arrival counters (zero between launches)
+    int rows, N, K, kpr, cms;
+    int tiles_m, tiles_n, split, segs_per_split, group_n, total_work;
+};
+
+struct QuantArgs {
+    const float* x;
+    uint8_t* q;
+    uint8_t* s;
+    int64_t rows, cols, ld_x, ld_q, ld_s;
+};
+
+hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
+hipError_t launch_gemm(int cfg, const GemmArgs& a, int grid, hipStream_t stream);
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
+}  // namespace mxg

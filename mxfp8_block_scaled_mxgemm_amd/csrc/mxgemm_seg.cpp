@@ -1,0 +1,551 @@
+// Host side of the segmented MXFP8 GEMM: argument rules, the launch plan,
+// the staging ring with its ready/credit events, and the C ABI.
+#include "mxgemm_seg.h"
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "schedule.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+    do {                                                                                \
+        hipError_t e_ = (expr);                                                         \
+        if (e_ != hipSuccess)                                                           \
+            return fail(MXGEMM_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));    \
+    } while (0)
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Argument rules (see the header for their sources).
+int validate(int64_t M, int64_t kpr, int32_t R, int64_t N, int64_t cms, int32_t nbuf)
+{
+    if (M <= 0 || kpr <= 0 || R <= 0 || N <= 0 || cms <= 0 || nbuf <= 0)
+        return fail(MXGEMM_EINVAL, "all sizes must be positive (M=%lld kPerRank=%lld R=%d N=%lld "
+                    "commMSize=%lld buffers=%d)", (long long)M, (long long)kpr, R, (long long)N,
+                    (long long)cms, nbuf);
+    if (R > 64)
+        return fail(MXGEMM_EINVAL, "rank_size %d exceeds 64", R);
+    if (!is_pow2(nbuf) || nbuf > 64)
+        return fail(MXGEMM_EINVAL, "buffer_count %d must be a power of two in [1, 64]", nbuf);
+    if (M % cms != 0)
+        return fail(MXGEMM_EINVAL, "commMSize %lld must divide M %lld (chunks have no tail)",
+                    (long long)cms, (long long)M);
+    if (kpr % 32 != 0)
+        return fail(MXGEMM_EINVAL, "kPerRank %lld must be a multiple of the MX block 32",
+                    (long long)kpr);
+    if (kpr % 128 != 0)
+        return fail(MXGEMM_EUNSUPPORTED, "kPerRank %lld must be a multiple of 128 (one MFMA "
+                    "K-step) in this build", (long long)kpr);
+    const int64_t K = (int64_t)R * kpr;
+    if (K > (1 << 22) || N >= (1LL << 31) || M >= (1LL << 31))
+        return fail(MXGEMM_EUNSUPPORTED, "problem too large for 32-bit tile offsets");
+    const int64_t ring = (int64_t)nbuf * R * cms * kpr;
+    if (ring >= (1LL << 31))
+        return fail(MXGEMM_EUNSUPPORTED, "staging ring of %lld bytes exceeds 2 GiB", (long long)ring);
+    if ((M / cms) > (1 << 30))
+        return fail(MXGEMM_EUNSUPPORTED, "too many chunks");
+    return MXGEMM_OK;
+}
+
+struct Choice {
+    int cfg, split;
+    double cost;
+};
+
+// Estimated time (arbitrary units) of one window under (cfg, split).
+double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int split,
+                int num_cus)
+{
+    const int64_t tiles = ceil_div(rows, t.tile_m) * ceil_div(N, t.tile_n);
+    const int64_t work = tiles * split;
+    const int64_t cap = (int64_t)num_cus * t.blocks_per_cu;
+    const int64_t rounds = ceil_div(work, cap);
+    // one work item: MFMA cycles at the tile's efficiency, sharing the CU
+    // with the other resident work-groups, plus fixed start-up cost
+    const double flops = 2.0 * t.tile_m * t.tile_n * (double)(K / split);
+    double item = flops / (8192.0 * t.rel_rate) * t.blocks_per_cu + 3000.0;
+    if (split > 1)
+        item += (double)t.tile_m * t.tile_n * 4.0 * 3.0 / 64.0;   // partial write + fix-up
+    return (double)rounds * item;
+}
+
+int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N, int64_t cms,
+              int32_t nbuf, int32_t num_cus, const mxgemm_seg_options_t* opts)
+{
+    int rc = validate(M, kpr, R, N, cms, nbuf);
+    if (rc != MXGEMM_OK)
+        return rc;
+    if (num_cus <= 0)
+        return fail(MXGEMM_EINVAL, "num_cus must be positive");
+    memset(p, 0, sizeof(*p));
+    p->M = M;
+    p->kPerRank = kpr;
+    p->N = N;
+    p->K = (int64_t)R * kpr;
+    p->commMSize = cms;
+    p->rank_size = R;
+    p->buffer_count = nbuf;
+    p->chunks = (int32_t)(M / cms);
+    p->num_cus = num_cus;
+
+    int W = nbuf > 1 ? nbuf / 2 : 1;
+    if (opts && opts->chunks_per_window > 0) {
+        if (nbuf % opts->chunks_per_window != 0)
+            return fail(MXGEMM_EINVAL, "chunks_per_window %d must divide buffer_count %d",
+                        opts->chunks_per_window, nbuf);
+        W = opts->chunks_per_window;
+    }
+    p->chunks_per_window = W;
+    p->windows = (int32_t)ceil_div(p->chunks, W);
+    p->window_slots = nbuf / W;
+    const int64_t rows = (int64_t)W * cms;
+
+    Choice best = {-1, 1, 1e300};
+    const int ncfg = mxg::num_tile_cfgs();
+    for (int c = 0; c < ncfg; ++c) {
+        if (opts && opts->tile_cfg >= 0 && opts->tile_cfg != c)
+            continue;
+        for (int s = 1; s <= R; ++s) {
+            if (R % s != 0)
+                continue;
+            if (opts && opts->split > 0 && opts->split != s)
+                continue;
+            const double cost = estimate(mxg::tile_cfg(c), rows, N, p->K, s, num_cus);
+            if (cost < best.cost * 0.999) {
+                best.cfg = c;
+                best.split = s;
+                best.cost = cost;
+            }
+        }
+    }
+    if (opts && opts->tile_cfg >= ncfg)
+        return fail(MXGEMM_EINVAL, "tile_cfg %d out of range [0, %d)", opts->tile_cfg, ncfg);
+    if (best.cfg < 0)
+        return fail(MXGEMM_EINVAL, "no plan satisfies the options (split must divide rank_size)");
+
+    const mxg::TileCfg& t = mxg::tile_cfg(best.cfg);
+    p->tile_cfg = best.cfg;
+    p->tile_m = t.tile_m;
+    p->tile_n = t.tile_n;
+    p->split = best.split;
+    p->tiles_m = (int32_t)ceil_div(rows, t.tile_m);
+    p->tiles_n = (int32_t)ceil_div(N, t.tile_n);
+    const int64_t work = (int64_t)p->tiles_m * p->tiles_n * p->split;
+    if (work >= (1LL << 31))
+        return fail(MXGEMM_EUNSUPPORTED, "too many work items");
+    p->work_items = (int32_t)work;
+    int64_t grid = (int64_t)num_cus * t.blocks_per_cu;
+    if (opts && opts->grid > 0 && opts->grid < grid)
+        grid = opts->grid;
+    p->grid = (int32_t)(work < grid ? work : grid);
+    // zigzag group width: about a square patch of tiles per XCD per round
+    const int64_t per_xcd = ceil_div(p->grid, mxg::kNumXcd) / p->split;
+    int g = (int)floor(sqrt((double)(per_xcd > 1 ? per_xcd : 1)));
+    if (g < 1)
+        g = 1;
+    if (g > p->tiles_n)
+        g = p->tiles_n;
+    p->group_n = g;
+    p->slot_bytes = (int64_t)R * cms * kpr;
+    p->scale_slot_bytes = (int64_t)R * cms * (kpr / 32);
+    p->workspace_bytes = p->split > 1
+        ? (int64_t)p->tiles_m * p->tiles_n * p->split * t.tile_m * t.tile_n * 4 : 0;
+    p->counter_count = (int64_t)p->tiles_m * p->tiles_n;
+    return MXGEMM_OK;
+}
+
+}  // namespace
+
+struct mxgemm_seg {
+    mxgemm_seg_plan_t plan;
+    int device;
+    uint8_t* ring;
+    uint8_t* sring;
+    float* ws;
+    int* counters;
+    hipStream_t side;
+    hipEvent_t start;
+    std::vector<hipEvent_t> ready, credit;
+    // measurement
+    bool profiling;
+    bool pending;
+    std::vector<hipEvent_t> gemm_ev, stage_ev;
+    double gemm_ms, stage_ms;
+    int gemm_n, stage_n;
+};
+
+namespace {
+
+void release(mxgemm_seg* h)
+{
+    if (h->side)
+        (void)hipStreamSynchronize(h->side);
+    for (hipEvent_t e : h->ready)
+        (void)hipEventDestroy(e);
+    for (hipEvent_t e : h->credit)
+        (void)hipEventDestroy(e);
+    for (hipEvent_t e : h->gemm_ev)
+        (void)hipEventDestroy(e);
+    for (hipEvent_t e : h->stage_ev)
+        (void)hipEventDestroy(e);
+    if (h->start)
+        (void)hipEventDestroy(h->start);
+    if (h->side)
+        (void)hipStreamDestroy(h->side);
+    if (h->ring)
+        (void)hipFree(h->ring);
+    if (h->sring)
+        (void)hipFree(h->sring);
+    if (h->ws)
+        (void)hipFree(h->ws);
+    if (h->counters)
+        (void)hipFree(h->counters);
+    delete h;
+}
+
+int harvest(mxgemm_seg* h)
+{
+    if (!h->pending)
+        return MXGEMM_OK;
+    h->pending = false;
+    const int nw = h->plan.windows;
+    HIP_TRY(hipEventSynchronize(h->gemm_ev[2 * nw - 1]));
+    HIP_TRY(hipEventSynchronize(h->stage_ev[2 * nw - 1]));
+    for (int w = 0; w < nw; ++w) {
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, h->gemm_ev[2 * w], h->gemm_ev[2 * w + 1]));
+        h->gemm_ms += ms;
+        HIP_TRY(hipEventElapsedTime(&ms, h->stage_ev[2 * w], h->stage_ev[2 * w + 1]));
+        h->stage_ms += ms;
+    }
+    h->gemm_n += nw;
+    h->stage_n += nw;
+    return MXGEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxgemm_seg_last_error(void) { return g_err.c_str(); }
+
+const char* mxgemm_seg_version(void) { return "mxgemm_seg 0.1 (gfx950)"; }
+
+int mxgemm_seg_plan(mxgemm_seg_plan_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
+                    int64_t N, int64_t commMSize, int32_t buffer_count, int32_t num_cus,
+                    const mxgemm_seg_options_t* opts)
+{
+    if (!out)
+        return fail(MXGEMM_EINVAL, "out is NULL");
+    mxgemm_seg_plan_t p;
+    int rc = make_plan(&p, M, kPerRank, rank_size, N, commMSize, buffer_count, num_cus, opts);
+    if (rc == MXGEMM_OK)
+        *out = p;
+    return rc;
+}
+
+int mxgemm_seg_decode(const mxgemm_seg_plan_t* plan, int64_t rows, int32_t w, int32_t block,
+                      int32_t* tile_m_idx, int32_t* tile_n_idx, int32_t* split_idx,
+                      int32_t* first_work)
+{
+    if (!plan || rows <= 0 || rows > (int64_t)plan->chunks_per_window * plan->commMSize)
+        return fail(MXGEMM_EINVAL, "bad plan or rows");
+    const int tiles_m = (int)ceil_div(rows, plan->tile_m);
+    const int total = tiles_m * plan->tiles_n * plan->split;
+    const int grid = total < plan->grid ? total : plan->grid;
+    if (w < 0 || w >= total || block < 0 || block >= grid)
+        return fail(MXGEMM_EINVAL, "work item or block out of range");
+    const mxg::TileCoord c = mxg::decode_work(w, tiles_m, plan->tiles_n, plan->split, plan->group_n);
+    if (tile_m_idx)
+        *tile_m_idx = c.tm;
+    if (tile_n_idx)
+        *tile_n_idx = c.tn;
+    if (split_idx)
+        *split_idx = c.ks;
+    if (first_work)
+        *first_work = mxg::remap_block(block, grid);
+    return MXGEMM_OK;
+}
+
+int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
+                         int64_t N, int64_t commMSize, int32_t buffer_count,
+                         const mxgemm_seg_options_t* opts)
+{
+    if (!out)
+        return fail(MXGEMM_EINVAL, "out is NULL");
+    int rc = validate(M, kPerRank, rank_size, N, commMSize, buffer_count);
+    if (rc != MXGEMM_OK)
+        return rc;
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    hipDeviceProp_t prop;
+    HIP_TRY(hipGetDeviceProperties(&prop, dev));
+    if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(MXGEMM_EUNSUPPORTED, "device %d is %s; this library is built for gfx950",
+                    dev, prop.gcnArchName);
+    mxgemm_seg_plan_t plan;
+    rc = make_plan(&plan, M, kPerRank, rank_size, N, commMSize, buffer_count,
+                   prop.multiProcessorCount, opts);
+    if (rc != MXGEMM_OK)
+        return rc;
+
+    mxgemm_seg* h = new mxgemm_seg();
+    h->plan = plan;
+    h->device = dev;
+    auto oom = [&](const char* what, size_t bytes) {
+        release(h);
+        return fail(MXGEMM_ENOMEM, "allocating %s (%zu bytes) failed", what, bytes);
+    };
+    const size_t ring_bytes = (size_t)plan.buffer_count * plan.slot_bytes;
+    const size_t sring_bytes = (size_t)plan.buffer_count * plan.scale_slot_bytes;
+    if (hipMalloc((void**)&h->ring, ring_bytes) != hipSuccess)
+        return oom("staging ring", ring_bytes);
+    if (hipMalloc((void**)&h->sring, sring_bytes) != hipSuccess)
+        return oom("staging scale ring", sring_bytes);
+    if (plan.workspace_bytes > 0 && hipMalloc((void**)&h->ws, plan.workspace_bytes) != hipSuccess)
+        return oom("split-K workspace", plan.workspace_bytes);
+    const size_t cnt_bytes = (size_t)plan.counter_count * sizeof(int);
+    if (hipMalloc((void**)&h->counters, cnt_bytes) != hipSuccess)
+        return oom("split-K counters", cnt_bytes);
+    hipError_t e = hipMemset(h->counters, 0, cnt_bytes);
+    if (e == hipSuccess)
+        e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    if (e == hipSuccess)
+        e = hipEventCreateWithFlags(&h->start, hipEventDisableTiming);
+    h->ready.assign(plan.window_slots, nullptr);
+    h->credit.assign(plan.window_slots, nullptr);
+    for (int i = 0; e == hipSuccess && i < plan.window_slots; ++i) {
+        e = hipEventCreateWithFlags(&h->ready[i], hipEventDisableTiming);
+        if (e == hipSuccess)
+            e = hipEventCreateWithFlags(&h->credit[i], hipEventDisableTiming);
+    }
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        release(h);
+        return fail(MXGEMM_EHIP, "handle setup failed: %s", hipGetErrorString(e));
+    }
+    *out = h;
+    return MXGEMM_OK;
+}
+
+int mxgemm_seg_create(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
+                      int64_t N, int64_t commMSize, int32_t buffer_count)
+{
+    return mxgemm_seg_create_ex(out, M, kPerRank, rank_size, N, commMSize, buffer_count, nullptr);
+}
+
+int mxgemm_seg_get_plan(mxgemm_seg_t h, mxgemm_seg_plan_t* out)
+{
+    if (!h || !out)
+        return fail(MXGEMM_EINVAL, "NULL handle or out");
+    *out = h->plan;
+    return MXGEMM_OK;
+}
+
+int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const void* b,
+                   const void* b_scale, void* c, void* stream)
+{
+    if (!h)
+        return fail(MXGEMM_EINVAL, "NULL handle");
+    if (!a_seg || !a_scale || !b || !b_scale || !c)
+        return fail(MXGEMM_EINVAL, "NULL data pointer");
+    if (((uintptr_t)a_seg | (uintptr_t)b) & 15u)
+        return fail(MXGEMM_EINVAL, "a_seg and b must be 16-byte aligned");
+    if (((uintptr_t)a_scale | (uintptr_t)b_scale) & 3u)
+        return fail(MXGEMM_EINVAL, "a_scale and b_scale must be 4-byte aligned");
+    if ((uintptr_t)c & 1u)
+        return fail(MXGEMM_EINVAL, "c must be 2-byte aligned");
+    const mxgemm_seg_plan_t& P = h->plan;
+    hipStream_t st = (hipStream_t)stream;
+
+    if (h->profiling) {
+        int rc = harvest(h);
+        if (rc != MXGEMM_OK)
+            return rc;
+    }
+
+    // fork: the side stream starts after everything already on `stream`
+    HIP_TRY(hipEventRecord(h->start, st));
+    HIP_TRY(hipStreamWaitEvent(h->side, h->start, 0));
+
+    const mxg::TileCfg& t = mxg::tile_cfg(P.tile_cfg);
+    const int64_t cap = (int64_t)P.num_cus * t.blocks_per_cu;
+    for (int w = 0; w < P.windows; ++w) {
+        const int chunk0 = w * P.chunks_per_window;
+        const int left = P.chunks - chunk0;
+        const int nch = left < P.chunks_per_window ? left : P.chunks_per_window;
+        const int g = w % P.window_slots;
+
+        // producer: refill slot group g once the GEMM that last read it is done
+        if (w >= P.window_slots)
+            HIP_TRY(hipStreamWaitEvent(h->side, h->credit[g], 0));
+        mxg::StageArgs sa;
+        sa.a_seg = (const uint8_t*)a_seg;
+        sa.sa_seg = (const uint8_t*)a_scale;
+        sa.ring = h->ring;
+        sa.sring = h->sring;
+        sa.M = P.M;
+        sa.kpr = P.kPerRank;
+        sa.cms = P.commMSize;
+        sa.slot_bytes = P.slot_bytes;
+        sa.scale_slot_bytes = P.scale_slot_bytes;
+        sa.R = P.rank_size;
+        sa.chunk0 = chunk0;
+        sa.nch = nch;
+        sa.nbuf = P.buffer_count;
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->stage_ev[2 * w], h->side));
+        HIP_TRY(mxg::launch_stage(sa, h->side));
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->stage_ev[2 * w + 1], h->side));
+        HIP_TRY(hipEventRecord(h->ready[g], h->side));
+
+        // consumer: GEMM over the window once its chunks have landed
+        HIP_TRY(hipStreamWaitEvent(st, h->ready[g], 0));
+        const int64_t rows = (int64_t)nch * P.commMSize;
+        mxg::GemmArgs ga;
+        ga.a = h->ring + (int64_t)g * P.chunks_per_window * P.slot_bytes;
+        ga.as = h->sring + (int64_t)g * P.chunks_per_window * P.scale_slot_bytes;
+        ga.a_slot_stride = P.slot_bytes;
+        ga.as_slot_stride = P.scale_slot_bytes;
+        ga.b = (const uint8_t*)b;
+        ga.bs = (const uint8_t*)b_scale;
+        ga.c = (uint16_t*)c + (int64_t)chunk0 * P.commMSize * P.N;
+        ga.ws = h->ws;
+        ga.counters = h->counters;
+        ga.rows = (int)rows;
+        ga.N = (int)P.N;
+        ga.K = (int)P.K;
+        ga.kpr = (int)P.kPerRank;
+        ga.cms = (int)P.commMSize;
+        ga.tiles_m = (int)ceil_div(rows, P.tile_m);
+        ga.tiles_n = P.tiles_n;
+        ga.split = P.split;
+        ga.segs_per_split = P.rank_size / P.split;
+        ga.group_n = P.group_n;
+        ga.total_work = ga.tiles_m * ga.tiles_n * ga.split;
+        int64_t grid = ga.total_work < P.grid ? ga.total_work : P.grid;
+        if (grid > cap)
+            grid = cap;
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->gemm_ev[2 * w], st));
+        HIP_TRY(mxg::launch_gemm(P.tile_cfg, ga, (int)grid, st));
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
+        HIP_TRY(hipEventRecord(h->credit[g], st));
+    }
+    if (h->profiling)
+        h->pending = true;
+    return MXGEMM_OK;
+}
+
+int mxgemm_seg_destroy(mxgemm_seg_t h)
+{
+    if (!h)
+        return MXGEMM_OK;
+    hipError_t e = hipSuccess;
+    if (h->side)
+        e = hipStreamSynchronize(h->side);
+    if (e == hipSuccess)
+        e = hipDeviceSynchronize();
+    release(h);
+    if (e != hipSuccess)
+        return fail(MXGEMM_EHIP, "destroy: %s", hipGetErrorString(e));
+    return MXGEMM_OK;
+}
+
+int mxgemm_seg_set_profiling(mxgemm_seg_t h, int32_t enable)
+{
+    if (!h)
+        return fail(MXGEMM_EINVAL, "NULL handle");
+    if (enable && h->gemm_ev.empty()) {
+        const int n = 2 * h->plan.windows;
+        h->gemm_ev.assign(n, nullptr);
+        h->stage_ev.assign(n, nullptr);
+        for (int i = 0; i < n; ++i) {
+            HIP_TRY(hipEventCreate(&h->gemm_ev[i]));
+            HIP_TRY(hipEventCreate(&h->stage_ev[i]));
+        }
+    }
+    if (!enable) {
+        int rc = harvest(h);
+        if (rc != MXGEMM_OK)
+            return rc;
+    }
+    h->profiling = enable != 0;
+    return MXGEMM_OK;
+}
+
+int mxgemm_seg_kernel_times(mxgemm_seg_t h, double* gemm_ms, int32_t* gemm_launches,
+                            double* stage_ms, int32_t* stage_launches)
+{
+    if (!h)
+        return fail(MXGEMM_EINVAL, "NULL handle");
+    int rc = harvest(h);
+    if (rc != MXGEMM_OK)
+        return rc;
+    if (gemm_ms)
+        *gemm_ms = h->gemm_ms;
+    if (gemm_launches)
+        *gemm_launches = h->gemm_n;
+    if (stage_ms)
+        *stage_ms = h->stage_ms;
+    if (stage_launches)
+        *stage_launches = h->stage_n;
+    h->gemm_ms = h->stage_ms = 0.0;
+    h->gemm_n = h->stage_n = 0;
+    return MXGEMM_OK;
+}
+
+int mxgemm_quantize_mxfp8(const float* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                          int64_t ld_q, uint8_t* s, int64_t ld_s, void* stream)
+{
+    if (!x || !q || !s)
+        return fail(MXGEMM_EINVAL, "NULL pointer");
+    if (rows < 0 || cols < 0 || cols % 32 != 0)
+        return fail(MXGEMM_EINVAL, "cols must be a non-negative multiple of 32");
+    if (ld_x < cols || ld_q < cols || ld_s < cols / 32)
+        return fail(MXGEMM_EINVAL, "leading dimensions smaller than the row length");
+    if (ld_x % 4 != 0 || ld_q % 4 != 0 || ((uintptr_t)x & 15u) || ((uintptr_t)q & 3u))
+        return fail(MXGEMM_EINVAL, "x must be 16-byte aligned with ld_x % 4 == 0; q 4-byte "
+                    "aligned with ld_q % 4 == 0");
+    mxg::QuantArgs a;
+    a.x = x;
+    a.q = q;
+    a.s = s;
+    a.rows = rows;
+    a.cols = cols;
+    a.ld_x = ld_x;
+    a.ld_q = ld_q;
+    a.ld_s = ld_s;
+    HIP_TRY(mxg::launch_quantize(a, (hipStream_t)stream));
+    return MXGEMM_OK;
+}
+
+}  // extern "C"

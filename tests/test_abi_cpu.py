@@ -1,0 +1,133 @@
+"""CPU-only checks of the C ABI library: it loads, exports every function
+the header declares, enforces the argument rules, and its scheduler decode
+is a bijection onto the tile/split space (no GPU calls)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mxfp8_block_scaled_mxgemm_amd as pkg
+from mxfp8_block_scaled_mxgemm_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxgemm_seg.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxgemm_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = pkg.load()
+    declared = _declared_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(pkg.EXPORTED) == declared
+
+
+def test_version_and_empty_error():
+    lib = pkg.load()
+    assert b"gfx950" in lib.mxgemm_seg_version()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 256, 2, 256, 64, 2), pkg._lib.MXGEMM_EINVAL),        # empty M
+    ((128, 256, 2, 0, 64, 2), pkg._lib.MXGEMM_EINVAL),        # empty N
+    ((128, 256, 0, 256, 64, 2), pkg._lib.MXGEMM_EINVAL),      # no ranks
+    ((128, 256, 2, 256, 48, 2), pkg._lib.MXGEMM_EINVAL),      # commMSize does not divide M
+    ((128, 256, 2, 256, 64, 3), pkg._lib.MXGEMM_EINVAL),      # ring depth not a power of 2
+    ((128, 48, 2, 256, 64, 2), pkg._lib.MXGEMM_EINVAL),       # not a multiple of the MX block
+    ((128, 96, 2, 256, 64, 2), pkg._lib.MXGEMM_EUNSUPPORTED), # MX-aligned, not MFMA-aligned
+    ((1 << 20, 1 << 14, 64, 256, 1 << 14, 64), pkg._lib.MXGEMM_EUNSUPPORTED),  # huge ring
+])
+def test_plan_argument_rules(args, code):
+    with pytest.raises(pkg.MxgemmError) as ei:
+        pkg.plan(*args)
+    assert ei.value.code == code
+    assert pkg.last_error()
+
+
+def test_plan_options_rules():
+    with pytest.raises(pkg.MxgemmError):
+        pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(split=3))
+    with pytest.raises(pkg.MxgemmError):
+        pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(chunks_per_window=3))
+    with pytest.raises(pkg.MxgemmError):
+        pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(tile_cfg=99))
+    p = pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(tile_cfg=2, split=2, chunks_per_window=2))
+    assert (p.tile_cfg, p.split, p.chunks_per_window, p.windows) == (2, 2, 2, 1)
+
+
+def _check_bijection(p, rows):
+    tiles_m = -(-rows // p.tile_m)
+    total = tiles_m * p.tiles_n * p.split
+    grid = min(total, p.grid)
+    seen = set()
+    for w in range(total):
+        tm, tn, ks, _ = pkg.decode(p, rows, w, 0)
+        assert 0 <= tm < tiles_m and 0 <= tn < p.tiles_n and 0 <= ks < p.split
+        seen.add((tm, tn, ks))
+    assert len(seen) == total
+    # every work item is reached by exactly one block of the persistent grid
+    starts = [pkg.decode(p, rows, 0, b)[3] for b in range(grid)]
+    assert sorted(starts) == list(range(grid))
+    covered = sorted(w for s in starts for w in range(s, total, grid))
+    assert covered == list(range(total))
+
+
+@pytest.mark.parametrize("name", list(inputs.WORKLOADS))
+def test_schedule_bijection_on_workloads(name):
+    w = inputs.WORKLOADS[name]
+    p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
+    full = p.chunks_per_window * w.commMSize
+    _check_bijection(p, full)
+    last = (p.chunks - (p.windows - 1) * p.chunks_per_window) * w.commMSize
+    if last != full:
+        _check_bijection(p, last)
+
+
+@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("split", [1, 2, 3])
+def test_schedule_bijection_forced(cfg, split):
+    p = pkg.plan(120, 256, 6, 200, 24, 4, num_cus=16,
+                 opts=pkg.options(tile_cfg=cfg, split=split))
+    _check_bijection(p, p.chunks_per_window * 24)
+    _check_bijection(p, 24)
+
+
+def test_xcd_remap_groups_blocks_per_xcd():
+    # with a grid that is a multiple of 8, the blocks of XCD x (b % 8 == x)
+    # start from one contiguous run of logical work IDs
+    p = pkg.plan(8192, 1024, 8, 8192, 512, 4)
+    assert p.grid % 8 == 0
+    rows = p.chunks_per_window * 512
+    for x in range(8):
+        starts = sorted(pkg.decode(p, rows, 0, b)[3] for b in range(x, p.grid, 8))
+        assert starts == list(range(starts[0], starts[0] + len(starts)))
+
+
+def test_zigzag_reverses_m_on_odd_groups():
+    p = pkg.plan(4096, 896, 8, 4096, 512, 4, opts=pkg.options(tile_cfg=2, split=1))
+    rows = p.chunks_per_window * 512
+    tiles_m = rows // p.tile_m
+    seq = [pkg.decode(p, rows, w, 0)[:2] for w in range(tiles_m * p.tiles_n)]
+    g = p.group_n
+    first_group = [tm for tm, tn in seq[: g * tiles_m]]
+    second_group = [tm for tm, tn in seq[g * tiles_m: 2 * g * tiles_m]]
+    assert first_group[0] == 0 and first_group[-1] == tiles_m - 1
+    assert second_group[0] == tiles_m - 1 and second_group[-1] == 0
+    # consecutive groups meet at the same tile row
+    assert first_group[-1] == second_group[0]
+
+
+def test_plan_ring_geometry():
+    w = inputs.WORKLOADS["c5"]
+    p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
+    assert p.slot_bytes == w.R * w.commMSize * w.kPerRank
+    assert p.scale_slot_bytes == p.slot_bytes // 32
+    assert p.chunks == w.M // w.commMSize
+    assert p.window_slots * p.chunks_per_window == w.nbuf

@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Floating-point outputs must satisfy |gpu - oracle| <= 1e-2 + 8e-3 |oracle|;
+integer-valued cases and the quantiser's encodings must match bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mxfp8_block_scaled_mxgemm_amd import inputs
+from gpu_common import (custom_case, sample_entries, say, summary, torch_cuda, within_tol,
+                        workload_case)
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _case(name):
+    if name not in _CACHE:
+        _CACHE.clear()
+        say(f"[case] building inputs for {name}")
+        _CACHE[name] = workload_case(name)
+    return _CACHE[name]
+
+
+# ------------------------------------------------------------- quantiser --
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_gpu_quantizer_bit_exact(name):
+    torch_cuda()
+    case = _case(name)
+    say(f"[quant] {name} {case.w.describe()}")
+    assert case.quantizer_matches()
+
+
+def test_gpu_quantizer_edge_values():
+    torch = torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    x[rng.random(x.shape) < 0.02] *= 100.0
+    x[3, :32] = 0.0
+    x[4, 32:64] = -0.0
+    x[5, 64:96] = 448.0
+    x[6, 96:128] = np.float32(448.0) * np.float32(2.0 ** -20)
+    x[7, 128:160] = np.float32(1e-39)
+    x[8, 160:192] = np.float32(3.0e38)
+    x[9, 192:224] = np.linspace(-1, 1, 32, dtype=np.float32) * np.float32(2.0 ** -130)
+    # exact E4M3 ties after scaling: amax 448 -> e = 0, values on midpoints
+    x[10, :32] = np.array([448.0] + [1.0625, 1.1875, 3.0 * 2 ** -10, 2 ** -10, 5 * 2 ** -10,
+                                     -1.0625, 0.0] * 3 + [240.0, 208.0, 272.0, 0.0078125,
+                                                          -0.0078125, 0.5, -0.5, 0.25],
+                          dtype=np.float32)[:32]
+    # all fp32 bit patterns of every exponent with tie-producing low bits
+    bits = (np.arange(64 * 4 * 32, dtype=np.uint32) * np.uint32(0x00080000 + 0x8000)) & np.uint32(0x43FFFFFF)
+    x[11:15] = bits.view(np.float32).reshape(-1, 256)[:4]
+    q, s = pkg.quantize_mxfp8(torch.from_numpy(x).cuda())
+    qr, sr = oracle.quantize_mxfp8(x)
+    assert np.array_equal(s.cpu().numpy(), sr)
+    assert np.array_equal(q.cpu().numpy(), qr)
+
+
+def test_gpu_quantizer_strided_views():
+    torch = torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    x = np.random.default_rng(2).standard_normal((40, 320)).astype(np.float32)
+    xd = torch.from_numpy(x).cuda()
+    q = torch.zeros((40, 512), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((40, 32), dtype=torch.uint8, device="cuda")
+    pkg.quantize_mxfp8(xd[:, 64:256], q[:, 128:320], s[:, 4:10])
+    qr, sr = oracle.quantize_mxfp8(np.ascontiguousarray(x[:, 64:256]))
+    qn, sn = q.cpu().numpy(), s.cpu().numpy()
+    assert np.array_equal(qn[:, 128:320], qr) and np.array_equal(sn[:, 4:10], sr)
+    assert not qn[:, :128].any() and not qn[:, 320:].any()       # nothing outside the view
+    assert not sn[:, :4].any() and not sn[:, 10:].any()
+
+
+# ---------------------------------------------------------------- parity --
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c4"])
+def test_parity_full(name):
+    torch_cuda()
+    case = _case(name)
+    say(f"[parity-full] {name} {case.w.describe()}")
+    got = case.run_gpu().float().cpu().numpy()
+    ref = case.oracle_full()
+    say("  " + summary(got, ref))
+    bad, _ = within_tol(got, ref)
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_parity_sampled(name):
+    torch_cuda()
+    case = _case(name)
+    say(f"[parity-sampled] {name} {case.w.describe()}")
+    c = case.run_gpu()
+    got_all = c.float().cpu().numpy()
+    assert not np.isnan(got_all).any()            # every output written
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    w = case.w
+    p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
+    ms, ns = sample_entries(w.M, w.N, p.tile_m, p.tile_n, seed=w.seed)
+    # plus every chunk boundary row
+    extra = np.arange(0, w.M, w.commMSize)
+    ms = np.concatenate([ms, extra, np.maximum(extra - 1, 0)])
+    ns = np.concatenate([ns, np.arange(len(extra)) % w.N, (np.arange(len(extra)) * 7) % w.N])
+    ref = case.oracle_entries(ms, ns)
+    got = got_all[ms, ns]
+    say("  " + summary(got, ref))
+    bad, _ = within_tol(got, ref)
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("split", [1, 2, 3, 6])
+def test_parity_forced_tiles_ragged(cfg, split):
+    """Every tile configuration and split on a ragged shape: window rows
+    (24 per chunk) and N = 200 are not multiples of any tile."""
+    torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    key = "ragged"
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = custom_case(R=6, M=120, kpr=256, N=200, cms=24, nbuf=4, seed=7)
+    case = _CACHE[key]
+    say(f"[parity-forced] cfg={cfg} split={split}")
+    got = case.run_gpu(opts=pkg.options(tile_cfg=cfg, split=split)).float().cpu().numpy()
+    ref = case.oracle_full()
+    bad, _ = within_tol(got, ref)
+    assert not bad.any(), summary(got, ref)
+
+
+@pytest.mark.parametrize("W", [1, 2, 4])
+def test_parity_window_sizes(W):
+    torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    key = "windows"
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = custom_case(R=4, M=256, kpr=512, N=384, cms=32, nbuf=4, seed=8)
+    case = _CACHE[key]
+    say(f"[parity-window] W={W}")
+    got = case.run_gpu(opts=pkg.options(chunks_per_window=W)).float().cpu().numpy()
+    ref = case.oracle_full()
+    bad, _ = within_tol(got, ref)
+    assert not bad.any(), summary(got, ref)
+
+
+# ------------------------------------------------- exact / invariant cases --
+
+def _sign_case(R, M, kpr, N, cms, nbuf, density, seed):
+    import torch
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    from gpu_common import Case
+    w = inputs.Workload("sign", R, M, kpr, N, cms, nbuf, 1.0, 0.0, 1.0, seed)
+    xa = inputs.sparse_sign_matrix((M, R * kpr), density, seed)
+    xb = inputs.sparse_sign_matrix((N, R * kpr), density, seed + 1)
+    return Case(w, xa, xb), xa, xb
+
+
+@pytest.mark.parametrize("shape", [
+    (4, 1024, 1024, 2048, 256, 2, 0.06),      # the c2 geometry
+    (8, 64, 896, 2048, 8, 4, 0.03),           # the c4 geometry
+])
+def test_integer_data_bit_exact(shape):
+    torch = torch_cuda()
+    R, M, kpr, N, cms, nbuf, dens = shape
+    say(f"[integer] R={R} M={M} kpr={kpr} N={N}")
+    case, xa, xb = _sign_case(R, M, kpr, N, cms, nbuf, dens, 50 + R)
+    ref = xa.astype(np.int64) @ xb.astype(np.int64).T
+    assert np.abs(ref).max() <= 256             # exact in fp32 and bfloat16
+    got = case.run_gpu().float().cpu().numpy()
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_k_split_invariance_gpu():
+    """Same logical A and B, K = 7168 split as (R, kPerRank) in four ways:
+    integer data gives identical bits, random data stays within tolerance
+    of the (split-independent) oracle."""
+    torch = torch_cuda()
+    M, N, K = 64, 512, 7168
+    xa = inputs.sparse_sign_matrix((M, K), 0.02, 61)
+    xb = inputs.sparse_sign_matrix((N, K), 0.02, 62)
+    rng = np.random.default_rng(63)
+    ra = rng.standard_normal((M, K)).astype(np.float32)
+    rb = rng.standard_normal((N, K)).astype(np.float32)
+    from gpu_common import Case
+    outs_i, outs_r = [], []
+    for R, kpr in ((8, 896), (4, 1792), (2, 3584), (1, 7168)):
+        say(f"[k-split] R={R}")
+        w = inputs.Workload("ks", R, M, kpr, N, 8, 4, 1.0, 0.0, 1.0, 0)
+        outs_i.append(Case(w, xa, xb).run_gpu().float().cpu().numpy())
+        cr = Case(w, ra, rb)
+        outs_r.append(cr.run_gpu().float().cpu().numpy())
+    ref_r = cr.oracle_full()
+    for o in outs_i[1:]:
+        assert np.array_equal(o, outs_i[0])
+    for o in outs_r:
+        bad, _ = within_tol(o, ref_r)
+        assert not bad.any()
+
+
+def test_scale_shift_law_gpu():
+    """Adding t to every A scale byte multiplies C by exactly 2^t."""
+    torch = torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    case = custom_case(R=4, M=128, kpr=512, N=256, cms=32, nbuf=2, seed=71)
+    w = case.w
+    c0 = case.run_gpu().float().cpu().numpy()
+    for t in (-3, 2):
+        a_s2 = (case.a_s.to(torch.int32) + t).to(torch.uint8)
+        c1 = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        with pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf) as g:
+            g.run(case.a_q, a_s2, case.b_q, case.b_s, c1)
+            torch.cuda.synchronize()
+        assert np.array_equal(c1.float().cpu().numpy(), c0 * np.float32(2.0 ** t))
+
+
+@pytest.mark.parametrize("operand", ["A", "B"])
+def test_one_block_scale_probe_gpu(operand):
+    """Integer data; shifting the scale of ONE 32-element block changes only
+    the outputs that block feeds, by exactly (2^t - 1) times its
+    contribution.  This pins which MFMA lane applies which scale byte."""
+    torch = torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    R, M, kpr, N, cms, nbuf = 2, 32, 256, 64, 16, 2
+    case, xa, xb = _sign_case(R, M, kpr, N, cms, nbuf, 0.5, 81)
+    w = case.w
+    base = case.run_gpu().float().cpu().numpy()
+    assert np.array_equal(base, (xa.astype(np.int64) @ xb.astype(np.int64).T).astype(np.float32))
+    assert np.abs(base).max() <= 64             # stays exact after a x4 block
+    t = 2
+    for (r, row, blk) in ((0, 5, 0), (1, 17, 3), (1, 31, 7), (0, 0, 5)):
+        kg0 = r * kpr + blk * 32
+        c1 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        a_s, b_s = case.a_s.clone(), case.b_s.clone()
+        if operand == "A":
+            a_s[r, row, blk] += t
+        else:
+            b_s[row, kg0 // 32] += t
+        with pkg.SegGemm(M, kpr, R, N, cms, nbuf) as g:
+            g.run(case.a_q, a_s, case.b_q, b_s, c1)
+            torch.cuda.synchronize()
+        got = c1.float().cpu().numpy()
+        exp = base.copy()
+        if operand == "A":
+            contrib = xb[:, kg0:kg0 + 32].astype(np.int64) @ xa[row, kg0:kg0 + 32].astype(np.int64)
+            exp[row, :] += (2 ** t - 1) * contrib
+        else:
+            contrib = xa[:, kg0:kg0 + 32].astype(np.int64) @ xb[row, kg0:kg0 + 32].astype(np.int64)
+            exp[:, row] += (2 ** t - 1) * contrib
+        assert np.array_equal(got, exp), (operand, r, row, blk)
