@@ -46,6 +46,20 @@ enum {
 
 typedef struct mxgemm_seg* mxgemm_seg_t;
 
+/* Arithmetic of the GEMM core.
+ *  MXGEMM_PRECISION_EXACT (default): every E4M3 x E4M3 x 2^(scales) product
+ *    is formed exactly (codes are converted to bfloat16 with the block scale
+ *    folded in, which is exact) and summed with FP32-grade accumulation on
+ *    v_mfma_f32_16x16x32_bf16.  Meets |C - exact| <= 1e-2 + 8e-3 |exact| on
+ *    any finite data whose sums stay in FP32 range.
+ *  MXGEMM_PRECISION_NATIVE: the CDNA4 block-scaled FP8 MFMA
+ *    (v_mfma_scale_f32_16x16x128_f8f6f4) at twice the peak rate.  Its
+ *    internal block dot drops products that are ~2^13 times smaller than
+ *    another product of the same group of eight, so data with large in-block
+ *    dynamic range (outliers) can miss the tolerance above where C is
+ *    small. */
+enum { MXGEMM_PRECISION_EXACT = 0, MXGEMM_PRECISION_NATIVE = 1 };
+
 /* Plan chosen for a problem: filled by mxgemm_seg_plan (host only, no GPU)
  * and by mxgemm_seg_get_plan for a live handle. */
 typedef struct mxgemm_seg_plan {
@@ -63,6 +77,8 @@ typedef struct mxgemm_seg_plan {
     int32_t grid;              /* persistent work-groups per GEMM launch    */
     int32_t group_n;           /* N-tiles per zigzag group                  */
     int32_t num_cus;
+    int32_t precision;         /* MXGEMM_PRECISION_*                        */
+    int32_t reserved;
     int64_t slot_bytes;        /* one staging buffer: R*commMSize*kPerRank  */
     int64_t scale_slot_bytes;  /* its scales: R*commMSize*kPerRank/32       */
     int64_t workspace_bytes;   /* FP32 split-K partials                     */
@@ -75,6 +91,7 @@ typedef struct mxgemm_seg_options {
     int32_t split;             /* force S (must divide rank_size)           */
     int32_t chunks_per_window; /* force W (must divide buffer_count)        */
     int32_t grid;              /* cap the persistent grid                   */
+    int32_t precision;         /* MXGEMM_PRECISION_* (-1 = EXACT)           */
 } mxgemm_seg_options_t;
 
 /*

@@ -44,7 +44,7 @@ class Plan(ctypes.Structure):
         ("tile_cfg", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
         ("split", ctypes.c_int32), ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
         ("work_items", ctypes.c_int32), ("grid", ctypes.c_int32), ("group_n", ctypes.c_int32),
-        ("num_cus", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32), ("precision", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("slot_bytes", ctypes.c_int64), ("scale_slot_bytes", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64), ("counter_count", ctypes.c_int64),
     ]
@@ -53,13 +53,18 @@ class Plan(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+PRECISION_EXACT = 0
+PRECISION_NATIVE = 1
+
+
 class Options(ctypes.Structure):
     _fields_ = [("tile_cfg", ctypes.c_int32), ("split", ctypes.c_int32),
-                ("chunks_per_window", ctypes.c_int32), ("grid", ctypes.c_int32)]
+                ("chunks_per_window", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("precision", ctypes.c_int32)]
 
 
-def options(tile_cfg=-1, split=-1, chunks_per_window=-1, grid=-1) -> Options:
-    return Options(tile_cfg, split, chunks_per_window, grid)
+def options(tile_cfg=-1, split=-1, chunks_per_window=-1, grid=-1, precision=-1) -> Options:
+    return Options(tile_cfg, split, chunks_per_window, grid, precision)
 
 
 _lib = None

@@ -53,7 +53,7 @@ struct QuantArgs {
 };
 
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
-hipError_t launch_gemm(int cfg, const GemmArgs& a, int grid, hipStream_t stream);
+hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, int grid, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 
 }  // namespace mxg

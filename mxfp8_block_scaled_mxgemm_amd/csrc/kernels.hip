@@ -12,7 +12,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // ----------------------------------------------------------------- table --
 
 // MFMA K-step: one v_mfma_scale_f32_16x16x128_f8f6f4 consumes 128 K per
-// row, i.e. four 32-element MX blocks.
+// row, i.e. four 32-element MX blocks.  Operand layout (measured with a
+// one-wave probe of the builtin): lane l holds row (or column) l % 16; with
+// q = l / 16 its 32 bytes are K [16q, 16q + 16) followed by K
+// [64 + 16q, 64 + 16q + 16), and its scale byte applies to MX block q, i.e.
+// K [32q, 32q + 32).  The result is D[4 * (l / 16) + v][l % 16] in
+// accumulator element v.
 constexpr int kBK = 128;
 
 template <int BM, int BN>
@@ -91,12 +96,36 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// E8M0 scale byte -> 2^(s - 127) as float (s = 0 is the float32 subnormal
+// 2^-127; 0xFF is NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s)
+{
+    s &= 0xFFu;
+    if (s == 0xFFu)
+        return __uint_as_float(0x7FC00000u);
+    return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+}
+
+// Eight E4M3 codes -> eight bfloat16 values times `scale`, in order.
+__device__ __forceinline__ v8bf fp8x8_to_bf16(u32x2 raw, float scale)
+{
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, true);
+    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
 // LDS tile rows are kBK = 128 bytes = eight 16-byte chunks.  The chunk
 // position is XOR-swizzled with the row so that the 16 lanes reading the
 // same K chunk of 16 consecutive rows hit different banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
-template <int BM, int BN, int WGM, int WGN, int OCC>
+template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 mxgemm_kernel(GemmArgs p)
 {
@@ -241,30 +270,61 @@ mxgemm_kernel(GemmArgs p)
             const uint8_t* ssa = sb_ + B_BYTES;
             const uint8_t* ssb = ssa + 4 * BM;
 
-            v8i bf[GB];
-            int sbv[GB];
+            if constexpr (!EXACT) {
+                v8i bf[GB];
+                int sbv[GB];
+    #pragma unroll
+                for (int j = 0; j < GB; ++j) {
+                    const int row = wn * TN + j * 16 + l16;
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(sb_ + row * kBK + swz(row, kb) * 16);
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(sb_ + row * kBK + swz(row, kb + 4) * 16);
+                    bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    sbv[j] = ssb[row * 4 + kb];
+                }
+    #pragma unroll
+                for (int i = 0; i < GA; ++i) {
+                    const int row = wm * TM + i * 16 + l16;
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(sa_ + row * kBK + swz(row, kb) * 16);
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(sa_ + row * kBK + swz(row, kb + 4) * 16);
+                    const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    const int sav = ssa[row * 4 + kb];
+    #pragma unroll
+                    for (int j = 0; j < GB; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            af, bf[j], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/,
+                            0, sav, 0, sbv[j]);
+                }
+            } else {
+                // Exact accumulation: each MX block j of the K-step is one
+                // v_mfma_f32_16x16x32_bf16.  Lane group q of a 16-row group
+                // takes 8 codes of block j (K [32j + 8q, 32j + 8q + 8)),
+                // converted to bfloat16 with the block's scale folded in
+                // (exact: 4-bit significands times a power of two).  A and
+                // B use the same K assignment, so every product pairs
+                // correctly; the products are exact in the MFMA and summed
+                // with FP32-grade precision.
 #pragma unroll
-            for (int j = 0; j < GB; ++j) {
-                const int row = wn * TN + j * 16 + l16;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(sb_ + row * kBK + swz(row, 2 * kb) * 16);
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(sb_ + row * kBK + swz(row, 2 * kb + 1) * 16);
-                bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                            (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                sbv[j] = ssb[row * 4 + kb];
-            }
+                for (int j = 0; j < 4; ++j) {
+                    const int ch = 2 * j + (kb >> 1), half = (kb & 1) * 8;
+                    v8bf bb[GB];
 #pragma unroll
-            for (int i = 0; i < GA; ++i) {
-                const int row = wm * TM + i * 16 + l16;
-                const u32x4 lo = *reinterpret_cast<const u32x4*>(sa_ + row * kBK + swz(row, 2 * kb) * 16);
-                const u32x4 hi = *reinterpret_cast<const u32x4*>(sa_ + row * kBK + swz(row, 2 * kb + 1) * 16);
-                const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                const int sav = ssa[row * 4 + kb];
+                    for (int g = 0; g < GB; ++g) {
+                        const int row = wn * TN + g * 16 + l16;
+                        const u32x2 raw = *reinterpret_cast<const u32x2*>(sb_ + row * kBK + swz(row, ch) * 16 + half);
+                        bb[g] = fp8x8_to_bf16(raw, e8m0_to_f32(ssb[row * 4 + j]));
+                    }
 #pragma unroll
-                for (int j = 0; j < GB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        af, bf[j], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/,
-                        0, sav, 0, sbv[j]);
+                    for (int i = 0; i < GA; ++i) {
+                        const int row = wm * TM + i * 16 + l16;
+                        const u32x2 raw = *reinterpret_cast<const u32x2*>(sa_ + row * kBK + swz(row, ch) * 16 + half);
+                        const v8bf ab = fp8x8_to_bf16(raw, e8m0_to_f32(ssa[row * 4 + j]));
+#pragma unroll
+                        for (int g = 0; g < GB; ++g)
+                            acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bb[g], acc[i][g], 0, 0, 0);
+                    }
+                }
             }
 
             if (s + 1 < nsteps)
@@ -340,21 +400,25 @@ mxgemm_kernel(GemmArgs p)
 }
 
 template <int BM, int BN, int WGM, int WGN, int OCC>
-static hipError_t launch_cfg(const GemmArgs& a, int grid, hipStream_t stream)
+static hipError_t launch_cfg(const GemmArgs& a, int grid, bool exact, hipStream_t stream)
 {
-    hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC>), dim3(grid), dim3(WGM * WGN * 64), 0,
-                       stream, a);
+    if (exact)
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, true>), dim3(grid),
+                           dim3(WGM * WGN * 64), 0, stream, a);
+    else
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, false>), dim3(grid),
+                           dim3(WGM * WGN * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int cfg, const GemmArgs& a, int grid, hipStream_t stream)
+hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, int grid, hipStream_t stream)
 {
     switch (cfg) {
-    case 0: return launch_cfg<256, 128, 2, 2, 1>(a, grid, stream);
-    case 1: return launch_cfg<128, 128, 2, 2, 1>(a, grid, stream);
-    case 2: return launch_cfg<64, 64, 2, 2, 4>(a, grid, stream);
-    case 3: return launch_cfg<32, 64, 1, 4, 4>(a, grid, stream);
-    case 4: return launch_cfg<16, 64, 1, 4, 4>(a, grid, stream);
+    case 0: return launch_cfg<256, 128, 2, 2, 1>(a, grid, exact, stream);
+    case 1: return launch_cfg<128, 128, 2, 2, 1>(a, grid, exact, stream);
+    case 2: return launch_cfg<64, 64, 2, 2, 4>(a, grid, exact, stream);
+    case 3: return launch_cfg<32, 64, 1, 4, 4>(a, grid, exact, stream);
+    case 4: return launch_cfg<16, 64, 1, 4, 4>(a, grid, exact, stream);
     default: return hipErrorInvalidValue;
     }
 }

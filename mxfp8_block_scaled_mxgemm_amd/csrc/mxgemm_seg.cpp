@@ -79,7 +79,7 @@ struct Choice {
 
 // Estimated time (arbitrary units) of one window under (cfg, split).
 double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int split,
-                int num_cus)
+                int num_cus, bool exact)
 {
     const int64_t tiles = ceil_div(rows, t.tile_m) * ceil_div(N, t.tile_n);
     const int64_t work = tiles * split;
@@ -88,7 +88,8 @@ double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int s
     // one work item: MFMA cycles at the tile's efficiency, sharing the CU
     // with the other resident work-groups, plus fixed start-up cost
     const double flops = 2.0 * t.tile_m * t.tile_n * (double)(K / split);
-    double item = flops / (8192.0 * t.rel_rate) * t.blocks_per_cu + 3000.0;
+    const double peak = exact ? 4096.0 : 8192.0;   // FLOP per clock per CU
+    double item = flops / (peak * t.rel_rate) * t.blocks_per_cu + 3000.0;
     if (split > 1)
         item += (double)t.tile_m * t.tile_n * 4.0 * 3.0 / 64.0;   // partial write + fix-up
     return (double)rounds * item;
@@ -112,6 +113,13 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     p->buffer_count = nbuf;
     p->chunks = (int32_t)(M / cms);
     p->num_cus = num_cus;
+    p->precision = MXGEMM_PRECISION_EXACT;
+    if (opts && opts->precision >= 0) {
+        if (opts->precision != MXGEMM_PRECISION_EXACT && opts->precision != MXGEMM_PRECISION_NATIVE)
+            return fail(MXGEMM_EINVAL, "unknown precision mode %d", opts->precision);
+        p->precision = opts->precision;
+    }
+    const bool exact = p->precision == MXGEMM_PRECISION_EXACT;
 
     int W = nbuf > 1 ? nbuf / 2 : 1;
     if (opts && opts->chunks_per_window > 0) {
@@ -135,7 +143,7 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
                 continue;
             if (opts && opts->split > 0 && opts->split != s)
                 continue;
-            const double cost = estimate(mxg::tile_cfg(c), rows, N, p->K, s, num_cus);
+            const double cost = estimate(mxg::tile_cfg(c), rows, N, p->K, s, num_cus, exact);
             if (cost < best.cost * 0.999) {
                 best.cfg = c;
                 best.split = s;
@@ -455,7 +463,7 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
             grid = cap;
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[2 * w], st));
-        HIP_TRY(mxg::launch_gemm(P.tile_cfg, ga, (int)grid, st));
+        HIP_TRY(mxg::launch_gemm(P.tile_cfg, P.precision == MXGEMM_PRECISION_EXACT, ga, (int)grid, st));
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
         HIP_TRY(hipEventRecord(h->credit[g], st));
