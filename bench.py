@@ -31,6 +31,7 @@ if ROOT not in sys.path:
 
 METRIC = "MXFP8 segmented GEMM TFLOP/s and % of MI355X MX-FP8 MFMA peak"
 PEAK_FP8_TFLOPS = 5000.0       # MI355X dense FP8 / MXFP8 MFMA
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense BF16 MFMA (the exact mode's contraction)
 PEAK_HBM_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
 
@@ -100,7 +101,22 @@ def main():
     ap.add_argument("--tile-cfg", type=int, default=-1)
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--window", type=int, default=-1)
+    ap.add_argument("--precision", choices=["exact", "native"], default="exact",
+                    help="GEMM arithmetic (default exact: parity-green on every workload)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy 256 MiB device-to-device three times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the ranks of this "
@@ -132,8 +148,10 @@ def main():
     torch.cuda.synchronize()
 
     opts = None
-    if args.tile_cfg >= 0 or args.split > 0 or args.window > 0:
-        opts = pkg.options(tile_cfg=args.tile_cfg, split=args.split, chunks_per_window=args.window)
+    prec = pkg.PRECISION_EXACT if args.precision == "exact" else pkg.PRECISION_NATIVE
+    if args.tile_cfg >= 0 or args.split > 0 or args.window > 0 or prec != pkg.PRECISION_EXACT:
+        opts = pkg.options(tile_cfg=args.tile_cfg, split=args.split, chunks_per_window=args.window,
+                           precision=prec)
     g = pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts)
     plan = g.plan.as_dict()
     log(f"[bench] plan: {plan}")
@@ -210,6 +228,7 @@ def main():
     flops = float(w.flops)
     flops_per_launch = flops / plan["windows"]
     achieved = flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
+    kernel_peak = PEAK_BF16_TFLOPS if args.precision == "exact" else PEAK_FP8_TFLOPS
     log(f"[bench] kernels: gemm {gemm_ms_per_launch * 1e3:.2f} us/launch x{plan['windows']}, "
         f"stage {stage_ms_per_launch * 1e3:.2f} us/launch")
 
@@ -244,13 +263,16 @@ def main():
                  if not args.no_flush else "stream (HIP events per step, warm caches)",
         "graph_ms_per_step_median": round(graph_ms, 5) if graph_ms is not None else None,
         "wall_s_timed_loop_incl_flush": round(wall, 4),
+        "precision": args.precision,
         "roofline": {
             "bound": "mfma",
-            "kernel": "mxgemm_kernel",
+            "kernel": "mxgemm_kernel (" + ("bf16 MFMA, exact products" if args.precision == "exact"
+                                           else "scaled FP8 MFMA") + ")",
             "achieved": round(achieved, 3),
-            "peak": PEAK_FP8_TFLOPS,
+            "peak": kernel_peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "frac": round(achieved / kernel_peak, 4),
+            "frac_of_mxfp8_peak": round(achieved / PEAK_FP8_TFLOPS, 4),
             "traffic": traffic,
             "gemm_us_per_launch": round(gemm_ms_per_launch * 1e3, 3),
             "launches_per_step": plan["windows"],

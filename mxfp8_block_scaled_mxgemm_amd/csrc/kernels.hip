@@ -21,14 +21,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBK = 128;
 
 template <int BM, int BN>
-constexpr int lds_bytes_for() { return 2 * (BM * kBK + BN * kBK + 4 * BM + 4 * BN); }
+constexpr int lds_bytes_for()
+{
+    return 2 * (BM * kBK + BN * kBK + 4 * (BM > 64 ? BM : 64) + 4 * (BN > 64 ? BN : 64));
+}
 
 static const TileCfg kCfgs[] = {
-    {256, 128, 256, lds_bytes_for<256, 128>(), 1, 0.90f},
-    {128, 128, 256, lds_bytes_for<128, 128>(), 1, 0.75f},
-    {64, 64, 256, lds_bytes_for<64, 64>(), 4, 0.45f},
-    {32, 64, 256, lds_bytes_for<32, 64>(), 4, 0.30f},
-    {16, 64, 256, lds_bytes_for<16, 64>(), 4, 0.20f},
+    // rel_rate: measured throughput per CU relative to the 256x256 tile
+    {256, 256, 512, lds_bytes_for<256, 256>(), 1, 1.00f},
+    {256, 128, 256, lds_bytes_for<256, 128>(), 1, 0.69f},
+    {128, 128, 256, lds_bytes_for<128, 128>(), 1, 0.53f},
+    {64, 64, 256, lds_bytes_for<64, 64>(), 4, 0.30f},
+    {32, 64, 256, lds_bytes_for<32, 64>(), 4, 0.20f},
+    {16, 64, 256, lds_bytes_for<16, 64>(), 4, 0.12f},
 };
 
 int num_tile_cfgs() { return (int)(sizeof(kCfgs) / sizeof(kCfgs[0])); }
@@ -100,24 +105,23 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-// E8M0 scale byte -> 2^(s - 127) as float (s = 0 is the float32 subnormal
-// 2^-127; 0xFF is NaN).
+// E8M0 scale byte -> 2^(s - 127) as float, branch-free: v_ldexp_f32 gives
+// 2^-127 (a float32 subnormal) for s = 0; the NaN byte 0xFF comes out as
+// +inf.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s)
 {
-    s &= 0xFFu;
-    if (s == 0xFFu)
-        return __uint_as_float(0x7FC00000u);
-    return s ? __uint_as_float(s << 23) : __uint_as_float(0x00400000u);
+    return __builtin_amdgcn_ldexpf(0x1p-127f, (int)(s & 0xFFu));
 }
 
 // Eight E4M3 codes -> eight bfloat16 values times `scale`, in order.
 __device__ __forceinline__ v8bf fp8x8_to_bf16(u32x2 raw, float scale)
 {
-    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, false);
-    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, true);
-    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, false);
-    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, true);
-    return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.x, scale, true));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, false));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw.y, scale, true));
+    return __builtin_bit_cast(v8bf, r);
 }
 
 // LDS tile rows are kBK = 128 bytes = eight 16-byte chunks.  The chunk
@@ -125,23 +129,46 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(u32x2 raw, float scale)
 // same K chunk of 16 consecutive rows hit different banks.
 __device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
 
+// One 16-byte (or 4-byte) piece per lane, straight from global memory into
+// LDS at lds + 16 * lane (resp. 4 * lane); lds must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* g, void* lds)
+{
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds)
+{
+    __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// Block-scaled GEMM over one window of staged rows.
+//
+// Work-group tile BM x BN, WGM x WGN waves, K-step 128 (four MX blocks).
+// Each K-step's A and B tiles and their scale bytes are copied global ->
+// LDS by the load unit itself (global_load_lds), double-buffered, so the
+// next step's copy runs while the current one is multiplied and no
+// registers hold staged data.  A lane of a copy instruction writes 16 bytes
+// at lds_base + 16 * lane: eight lanes fill one 128-byte tile row, and lane
+// L fetches the logical chunk that the row's XOR swizzle places at physical
+// chunk L % 8.
 template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 mxgemm_kernel(GemmArgs p)
 {
-    constexpr int NT = WGM * WGN * 64;
+    constexpr int NW = WGM * WGN;
+    constexpr int NT = NW * 64;
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int GA = TM / 16, GB = TN / 16;
     static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows come in groups of 8");
     constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK;
-    constexpr int STAGE = A_BYTES + B_BYTES + 4 * BM + 4 * BN;
-    constexpr int CA = (BM * 8 + NT - 1) / NT;   // 16-byte A chunks per thread
-    constexpr int CB = (BN * 8 + NT - 1) / NT;
-    constexpr int SA = (BM + NT - 1) / NT;       // A scale dwords per thread
-    constexpr int SB = (BN + NT - 1) / NT;
-    constexpr bool A_FULL = (BM * 8) % NT == 0, B_FULL = (BN * 8) % NT == 0;
+    // scale bytes: 4 per row and K-step; padded to one 64-lane copy
+    constexpr int SA_BYTES = 4 * (BM > 64 ? BM : 64), SB_BYTES = 4 * (BN > 64 ? BN : 64);
+    constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+    constexpr int IA = BM / 8, IB = BN / 8;            // 1 KB copies per K-step
+    constexpr int JA = (IA + NW - 1) / NW, JB = (IB + NW - 1) / NW;
+    constexpr int ISA = (BM + 63) / 64, ISB = (BN + 63) / 64;   // scale copies
 
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
@@ -158,49 +185,48 @@ mxgemm_kernel(GemmArgs p)
         const TileCoord tc = decode_work(w, p.tiles_m, p.tiles_n, p.split, p.group_n);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
 
-        // Per-thread 32-bit row offsets for this tile.  A offsets are
-        // relative to the window's ring base (the ring is < 2 GiB), B
+        // Per-lane 32-bit source offsets of this wave's copies.  A offsets
+        // are relative to the window's ring base (the ring is < 2 GiB), B
         // offsets relative to row n0 of B.  Rows past the edge are clamped
         // to the last valid row; their results are never stored.
-        uint32_t a_off[CA], b_off[CB], as_off[SA], bs_off[SB];
+        uint32_t a_off[JA], b_off[JB], as_off[ISA], bs_off[ISB];
 #pragma unroll
-        for (int i = 0; i < CA; ++i) {
-            const int idx = tid + i * NT;
-            const int row = (idx >> 3) < BM ? (idx >> 3) : BM - 1, ch = idx & 7;
+        for (int j = 0; j < JA; ++j) {
+            const int t = wave + j * NW;                 // copy index
+            const int row = 8 * (t < IA ? t : IA - 1) + (lane >> 3);
+            const int ch = (lane & 7) ^ (row & 7);
             int g = m0 + row;
             g = g < p.rows ? g : p.rows - 1;
-            a_off[i] = (uint32_t)((g / p.cms) * p.a_slot_stride) + (uint32_t)((g % p.cms) * p.kpr) + ch * 16;
+            a_off[j] = (uint32_t)((g / p.cms) * p.a_slot_stride) + (uint32_t)((g % p.cms) * p.kpr) + ch * 16;
         }
 #pragma unroll
-        for (int i = 0; i < CB; ++i) {
-            const int idx = tid + i * NT;
-            const int row = (idx >> 3) < BN ? (idx >> 3) : BN - 1, ch = idx & 7;
-            int g = row;
-            g = n0 + g < p.N ? g : p.N - 1 - n0;
-            b_off[i] = (uint32_t)g * (uint32_t)p.K + ch * 16;
+        for (int j = 0; j < JB; ++j) {
+            const int t = wave + j * NW;
+            const int row = 8 * (t < IB ? t : IB - 1) + (lane >> 3);
+            const int ch = (lane & 7) ^ (row & 7);
+            int g = n0 + row < p.N ? row : p.N - 1 - n0;
+            b_off[j] = (uint32_t)g * (uint32_t)p.K + ch * 16;
         }
 #pragma unroll
-        for (int i = 0; i < SA; ++i) {
-            const int row = (tid + i * NT) < BM ? tid + i * NT : BM - 1;
+        for (int j = 0; j < ISA; ++j) {
+            int row = 64 * j + lane;
+            row = row < BM ? row : BM - 1;
             int g = m0 + row;
             g = g < p.rows ? g : p.rows - 1;
-            as_off[i] = (uint32_t)((g / p.cms) * p.as_slot_stride) + (uint32_t)((g % p.cms) * sk);
+            as_off[j] = (uint32_t)((g / p.cms) * p.as_slot_stride) + (uint32_t)((g % p.cms) * sk);
         }
 #pragma unroll
-        for (int i = 0; i < SB; ++i) {
-            const int row = (tid + i * NT) < BN ? tid + i * NT : BN - 1;
-            int g = row;
-            g = n0 + g < p.N ? g : p.N - 1 - n0;
-            bs_off[i] = (uint32_t)g * (uint32_t)K32;
+        for (int j = 0; j < ISB; ++j) {
+            int row = 64 * j + lane;
+            row = row < BN ? row : BN - 1;
+            int g = n0 + row < p.N ? row : p.N - 1 - n0;
+            bs_off[j] = (uint32_t)g * (uint32_t)K32;
         }
         const uint8_t* __restrict__ bt = p.b + (int64_t)n0 * p.K;
         const uint8_t* __restrict__ bst = p.bs + (int64_t)n0 * K32;
 
         const int seg0 = tc.ks * p.segs_per_split;
         const int nsteps = p.segs_per_split * steps_per_seg;
-
-        u32x4 ra[CA], rb[CB];
-        uint32_t rsa[SA], rsb[SB];
 
         v4f acc[GA][GB];
 #pragma unroll
@@ -209,92 +235,93 @@ mxgemm_kernel(GemmArgs p)
             for (int j = 0; j < GB; ++j)
                 acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-// global -> registers for K-step S of this split
-#define MXG_LOAD_STEP(S)                                                                   \
+// issue the copies of K-step S into stage buffer BUF
+#define MXG_COPY_STEP(S, BUF)                                                              \
     do {                                                                                   \
         const int seg_ = seg0 + (S) / steps_per_seg;                                       \
         const int kk_ = ((S) % steps_per_seg) * kBK;                                       \
-        const uint8_t* __restrict__ a_ = p.a + (int64_t)seg_ * p.cms * p.kpr + kk_;         \
-        const uint8_t* __restrict__ b_ = bt + (int64_t)seg_ * p.kpr + kk_;                  \
-        const uint8_t* __restrict__ as_ = p.as + (int64_t)seg_ * p.cms * sk + (kk_ >> 5);   \
-        const uint8_t* __restrict__ bs_ = bst + (((int64_t)seg_ * p.kpr + kk_) >> 5);       \
-        _Pragma("unroll") for (int i = 0; i < CA; ++i)                                     \
-            ra[i] = *reinterpret_cast<const u32x4*>(a_ + a_off[i]);                        \
-        _Pragma("unroll") for (int i = 0; i < CB; ++i)                                     \
-            rb[i] = *reinterpret_cast<const u32x4*>(b_ + b_off[i]);                        \
-        _Pragma("unroll") for (int i = 0; i < SA; ++i)                                     \
-            rsa[i] = *reinterpret_cast<const uint32_t*>(as_ + as_off[i]);                  \
-        _Pragma("unroll") for (int i = 0; i < SB; ++i)                                     \
-            rsb[i] = *reinterpret_cast<const uint32_t*>(bs_ + bs_off[i]);                  \
-    } while (0)
-
-// registers -> LDS stage buffer BUF
-#define MXG_STORE_STEP(BUF)                                                                \
-    do {                                                                                   \
-        uint8_t* sa_ = smem + (BUF) * STAGE;                                               \
-        uint8_t* sb_ = sa_ + A_BYTES;                                                      \
-        uint32_t* ssa_ = reinterpret_cast<uint32_t*>(sb_ + B_BYTES);                       \
-        uint32_t* ssb_ = ssa_ + BM;                                                        \
-        _Pragma("unroll") for (int i = 0; i < CA; ++i) {                                   \
-            const int idx = tid + i * NT;                                                  \
-            const int row = idx >> 3, ch = idx & 7;                                        \
-            if (A_FULL || idx < BM * 8)                                                    \
-                *reinterpret_cast<u32x4*>(sa_ + row * kBK + swz(row, ch) * 16) = ra[i];    \
+        const uint8_t* a_ = p.a + (int64_t)seg_ * p.cms * p.kpr + kk_;                      \
+        const uint8_t* b_ = bt + (int64_t)seg_ * p.kpr + kk_;                               \
+        const uint8_t* as_ = p.as + (int64_t)seg_ * p.cms * sk + (kk_ >> 5);                \
+        const uint8_t* bs_ = bst + (((int64_t)seg_ * p.kpr + kk_) >> 5);                    \
+        uint8_t* st_ = smem + (BUF) * STAGE;                                               \
+        _Pragma("unroll") for (int j = 0; j < JA; ++j)                                     \
+            if (IA % NW == 0 || wave + j * NW < IA)                                        \
+                dma16(a_ + a_off[j], st_ + (wave + j * NW) * 1024);                        \
+        _Pragma("unroll") for (int j = 0; j < JB; ++j)                                     \
+            if (IB % NW == 0 || wave + j * NW < IB)                                        \
+                dma16(b_ + b_off[j], st_ + A_BYTES + (wave + j * NW) * 1024);              \
+        if (wave == 0) {                                                                   \
+            _Pragma("unroll") for (int j = 0; j < ISA; ++j)                                \
+                dma4(as_ + as_off[j], st_ + A_BYTES + B_BYTES + j * 256);                  \
         }                                                                                  \
-        _Pragma("unroll") for (int i = 0; i < CB; ++i) {                                   \
-            const int idx = tid + i * NT;                                                  \
-            const int row = idx >> 3, ch = idx & 7;                                        \
-            if (B_FULL || idx < BN * 8)                                                    \
-                *reinterpret_cast<u32x4*>(sb_ + row * kBK + swz(row, ch) * 16) = rb[i];    \
+        if (wave == NW - 1) {                                                              \
+            _Pragma("unroll") for (int j = 0; j < ISB; ++j)                                \
+                dma4(bs_ + bs_off[j], st_ + A_BYTES + B_BYTES + SA_BYTES + j * 256);       \
         }                                                                                  \
-        _Pragma("unroll") for (int i = 0; i < SA; ++i)                                     \
-            if (tid + i * NT < BM)                                                         \
-                ssa_[tid + i * NT] = rsa[i];                                               \
-        _Pragma("unroll") for (int i = 0; i < SB; ++i)                                     \
-            if (tid + i * NT < BN)                                                         \
-                ssb_[tid + i * NT] = rsb[i];                                               \
     } while (0)
 
         __syncthreads();   // the previous work item is done with the LDS
-        MXG_LOAD_STEP(0);
-        MXG_STORE_STEP(0);
+        MXG_COPY_STEP(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
         for (int s = 0; s < nsteps; ++s) {
             const int buf = s & 1;
             if (s + 1 < nsteps)
-                MXG_LOAD_STEP(s + 1);
+                MXG_COPY_STEP(s + 1, buf ^ 1);
 
             const uint8_t* sa_ = smem + buf * STAGE;
             const uint8_t* sb_ = sa_ + A_BYTES;
             const uint8_t* ssa = sb_ + B_BYTES;
-            const uint8_t* ssb = ssa + 4 * BM;
+            const uint8_t* ssb = ssa + SA_BYTES;
 
             if constexpr (!EXACT) {
+                // Native: one scaled MFMA per (A group, B group) per K-step.
+                // B fragments for the whole step first; A fragments double
+                // buffered so group i + 1 is in flight while group i's MFMAs
+                // run.
+                const int off_lo = l16 * kBK + swz(l16, kb) * 16;
+                const int off_hi = l16 * kBK + swz(l16, kb + 4) * 16;
+                const uint8_t* pa = sa_ + (wm * TM) * kBK;
+                const uint8_t* pb = sb_ + (wn * TN) * kBK;
+                const uint8_t* psa = ssa + (wm * TM + l16) * 4 + kb;
+                const uint8_t* psb = ssb + (wn * TN + l16) * 4 + kb;
                 v8i bf[GB];
                 int sbv[GB];
-    #pragma unroll
+#pragma unroll
                 for (int j = 0; j < GB; ++j) {
-                    const int row = wn * TN + j * 16 + l16;
-                    const u32x4 lo = *reinterpret_cast<const u32x4*>(sb_ + row * kBK + swz(row, kb) * 16);
-                    const u32x4 hi = *reinterpret_cast<const u32x4*>(sb_ + row * kBK + swz(row, kb + 4) * 16);
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + j * 16 * kBK + off_lo);
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + j * 16 * kBK + off_hi);
                     bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    sbv[j] = ssb[row * 4 + kb];
+                    sbv[j] = psb[j * 64];
                 }
-    #pragma unroll
+                v8i af[2];
+                int sav[2];
+                {
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + off_lo);
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + off_hi);
+                    af[0] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    sav[0] = psa[0];
+                }
+#pragma unroll
                 for (int i = 0; i < GA; ++i) {
-                    const int row = wm * TM + i * 16 + l16;
-                    const u32x4 lo = *reinterpret_cast<const u32x4*>(sa_ + row * kBK + swz(row, kb) * 16);
-                    const u32x4 hi = *reinterpret_cast<const u32x4*>(sa_ + row * kBK + swz(row, kb + 4) * 16);
-                    const v8i af = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    const int sav = ssa[row * 4 + kb];
-    #pragma unroll
+                    const int cur = i & 1;
+                    if (i + 1 < GA) {
+                        const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + (i + 1) * 16 * kBK + off_lo);
+                        const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + (i + 1) * 16 * kBK + off_hi);
+                        af[cur ^ 1] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        sav[cur ^ 1] = psa[(i + 1) * 64];
+                    }
+#pragma unroll
                     for (int j = 0; j < GB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            af, bf[j], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/,
-                            0, sav, 0, sbv[j]);
+                            af[cur], bf[j], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/,
+                            0, sav[cur], 0, sbv[j]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
                 // Exact accumulation: each MX block j of the K-step is one
@@ -304,35 +331,56 @@ mxgemm_kernel(GemmArgs p)
                 // (exact: 4-bit significands times a power of two).  A and
                 // B use the same K assignment, so every product pairs
                 // correctly; the products are exact in the MFMA and summed
-                // with FP32-grade precision.
+                // with FP32-grade precision.  Row r of a fragment group is
+                // r = group base + l16 with the group base a multiple of 16,
+                // so r & 7 = l16 & 7 and the swizzled byte offsets of a
+                // lane differ between groups by a constant.
+                //
+                // Per block j: all raw codes of the wave's A and B rows are
+                // read at once, B is converted, then group i + 1 of A is
+                // converted while group i's MFMAs run.
+                uint32_t sa_w[GA], sb_w[GB];
+#pragma unroll
+                for (int g = 0; g < GB; ++g)
+                    sb_w[g] = *reinterpret_cast<const uint32_t*>(ssb + (wn * TN + g * 16 + l16) * 4);
+#pragma unroll
+                for (int i = 0; i < GA; ++i)
+                    sa_w[i] = *reinterpret_cast<const uint32_t*>(ssa + (wm * TM + i * 16 + l16) * 4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int ch = 2 * j + (kb >> 1), half = (kb & 1) * 8;
+                    const int lane_off = l16 * kBK + swz(l16, 2 * j + (kb >> 1)) * 16 + (kb & 1) * 8;
+                    const uint8_t* pa = sa_ + (wm * TM) * kBK + lane_off;
+                    const uint8_t* pb = sb_ + (wn * TN) * kBK + lane_off;
+                    u32x2 rb[GB], ra[GA];
+#pragma unroll
+                    for (int g = 0; g < GB; ++g)
+                        rb[g] = *reinterpret_cast<const u32x2*>(pb + g * 16 * kBK);
+#pragma unroll
+                    for (int i = 0; i < GA; ++i)
+                        ra[i] = *reinterpret_cast<const u32x2*>(pa + i * 16 * kBK);
                     v8bf bb[GB];
 #pragma unroll
-                    for (int g = 0; g < GB; ++g) {
-                        const int row = wn * TN + g * 16 + l16;
-                        const u32x2 raw = *reinterpret_cast<const u32x2*>(sb_ + row * kBK + swz(row, ch) * 16 + half);
-                        bb[g] = fp8x8_to_bf16(raw, e8m0_to_f32(ssb[row * 4 + j]));
-                    }
+                    for (int g = 0; g < GB; ++g)
+                        bb[g] = fp8x8_to_bf16(rb[g], e8m0_to_f32(sb_w[g] >> (8 * j)));
+                    v8bf ab[2];
+                    ab[0] = fp8x8_to_bf16(ra[0], e8m0_to_f32(sa_w[0] >> (8 * j)));
 #pragma unroll
                     for (int i = 0; i < GA; ++i) {
-                        const int row = wm * TM + i * 16 + l16;
-                        const u32x2 raw = *reinterpret_cast<const u32x2*>(sa_ + row * kBK + swz(row, ch) * 16 + half);
-                        const v8bf ab = fp8x8_to_bf16(raw, e8m0_to_f32(ssa[row * 4 + j]));
+                        const int cur = i & 1;
 #pragma unroll
                         for (int g = 0; g < GB; ++g)
-                            acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bb[g], acc[i][g], 0, 0, 0);
+                            acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[cur], bb[g], acc[i][g], 0, 0, 0);
+                        if (i + 1 < GA)
+                            ab[cur ^ 1] = fp8x8_to_bf16(ra[i + 1], e8m0_to_f32(sa_w[i + 1] >> (8 * j)));
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                 }
             }
 
-            if (s + 1 < nsteps)
-                MXG_STORE_STEP(buf ^ 1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         }
-#undef MXG_LOAD_STEP
-#undef MXG_STORE_STEP
+#undef MXG_COPY_STEP
 
         // ---- epilogue --------------------------------------------------
         const int row_base = m0 + wm * TM + 4 * kb;
@@ -414,11 +462,12 @@ static hipError_t launch_cfg(const GemmArgs& a, int grid, bool exact, hipStream_
 hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, int grid, hipStream_t stream)
 {
     switch (cfg) {
-    case 0: return launch_cfg<256, 128, 2, 2, 1>(a, grid, exact, stream);
-    case 1: return launch_cfg<128, 128, 2, 2, 1>(a, grid, exact, stream);
-    case 2: return launch_cfg<64, 64, 2, 2, 4>(a, grid, exact, stream);
-    case 3: return launch_cfg<32, 64, 1, 4, 4>(a, grid, exact, stream);
-    case 4: return launch_cfg<16, 64, 1, 4, 4>(a, grid, exact, stream);
+    case 0: return launch_cfg<256, 256, 2, 4, 2>(a, grid, exact, stream);
+    case 1: return launch_cfg<256, 128, 2, 2, 1>(a, grid, exact, stream);
+    case 2: return launch_cfg<128, 128, 2, 2, 1>(a, grid, exact, stream);
+    case 3: return launch_cfg<64, 64, 2, 2, 4>(a, grid, exact, stream);
+    case 4: return launch_cfg<32, 64, 1, 4, 4>(a, grid, exact, stream);
+    case 5: return launch_cfg<16, 64, 1, 4, 4>(a, grid, exact, stream);
     default: return hipErrorInvalidValue;
     }
 }

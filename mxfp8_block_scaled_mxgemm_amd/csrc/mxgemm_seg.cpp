@@ -121,40 +121,63 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     }
     const bool exact = p->precision == MXGEMM_PRECISION_EXACT;
 
-    int W = nbuf > 1 ? nbuf / 2 : 1;
+    // Window size W (chunks per stage/GEMM launch pair).  W = nbuf / 2
+    // lets the staging of window w + 1 overlap the GEMM of window w; W =
+    // nbuf gives the GEMM twice the rows (bigger tiles, fuller grid) but the
+    // staging of each window then waits for the previous GEMM.  The plan
+    // takes the cheaper of the two under the cost model below.
+    int w_cand[2] = {nbuf > 1 ? nbuf / 2 : 1, nbuf};
+    int n_w = nbuf > 1 ? 2 : 1;
     if (opts && opts->chunks_per_window > 0) {
         if (nbuf % opts->chunks_per_window != 0)
             return fail(MXGEMM_EINVAL, "chunks_per_window %d must divide buffer_count %d",
                         opts->chunks_per_window, nbuf);
-        W = opts->chunks_per_window;
+        w_cand[0] = opts->chunks_per_window;
+        n_w = 1;
     }
+    if (opts && opts->tile_cfg >= mxg::num_tile_cfgs())
+        return fail(MXGEMM_EINVAL, "tile_cfg %d out of range [0, %d)", opts->tile_cfg,
+                    mxg::num_tile_cfgs());
+
+    Choice best = {-1, 1, 1e300};
+    int best_w = w_cand[0];
+    const int ncfg = mxg::num_tile_cfgs();
+    for (int wi = 0; wi < n_w; ++wi) {
+        const int W = w_cand[wi];
+        const int64_t windows = ceil_div(p->chunks, W);
+        const int64_t rows = (int64_t)W * cms;
+        // staging one window: read + write of its data and scales at an
+        // assumed 4 TB/s, in 2.4 GHz clock cycles
+        const double stage = 2.0 * (double)rows * R * kpr * 33.0 / 32.0 / 4.0e12 * 2.4e9;
+        const bool overlap = nbuf / W >= 2;
+        for (int c = 0; c < ncfg; ++c) {
+            if (opts && opts->tile_cfg >= 0 && opts->tile_cfg != c)
+                continue;
+            for (int s = 1; s <= R; ++s) {
+                if (R % s != 0)
+                    continue;
+                if (opts && opts->split > 0 && opts->split != s)
+                    continue;
+                const double gemm = estimate(mxg::tile_cfg(c), rows, N, p->K, s, num_cus, exact);
+                const double cost = overlap
+                    ? (double)windows * (gemm > stage ? gemm : stage) + stage
+                    : (double)windows * (gemm + stage);
+                if (cost < best.cost * 0.999) {
+                    best.cfg = c;
+                    best.split = s;
+                    best.cost = cost;
+                    best_w = W;
+                }
+            }
+        }
+    }
+    if (best.cfg < 0)
+        return fail(MXGEMM_EINVAL, "no plan satisfies the options (split must divide rank_size)");
+    const int W = best_w;
     p->chunks_per_window = W;
     p->windows = (int32_t)ceil_div(p->chunks, W);
     p->window_slots = nbuf / W;
     const int64_t rows = (int64_t)W * cms;
-
-    Choice best = {-1, 1, 1e300};
-    const int ncfg = mxg::num_tile_cfgs();
-    for (int c = 0; c < ncfg; ++c) {
-        if (opts && opts->tile_cfg >= 0 && opts->tile_cfg != c)
-            continue;
-        for (int s = 1; s <= R; ++s) {
-            if (R % s != 0)
-                continue;
-            if (opts && opts->split > 0 && opts->split != s)
-                continue;
-            const double cost = estimate(mxg::tile_cfg(c), rows, N, p->K, s, num_cus, exact);
-            if (cost < best.cost * 0.999) {
-                best.cfg = c;
-                best.split = s;
-                best.cost = cost;
-            }
-        }
-    }
-    if (opts && opts->tile_cfg >= ncfg)
-        return fail(MXGEMM_EINVAL, "tile_cfg %d out of range [0, %d)", opts->tile_cfg, ncfg);
-    if (best.cfg < 0)
-        return fail(MXGEMM_EINVAL, "no plan satisfies the options (split must divide rank_size)");
 
     const mxg::TileCfg& t = mxg::tile_cfg(best.cfg);
     p->tile_cfg = best.cfg;
