@@ -150,16 +150,36 @@ __device__ __forceinline__ void dma4(const void* g, void* lds)
 // at lds_base + 16 * lane: eight lanes fill one 128-byte tile row, and lane
 // L fetches the logical chunk that the row's XOR swizzle places at physical
 // chunk L % 8.
-template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT>
+//
+// MW is the MFMA width.  MW = 16: v_mfma_scale_f32_16x16x128_f8f6f4
+// (native) or v_mfma_f32_16x16x32_bf16 (exact).  MW = 32:
+// v_mfma_scale_f32_32x32x64_f8f6f4 (native) or v_mfma_f32_32x32x16_bf16
+// (exact); every 16-byte LDS read then feeds whole instructions.
+// Accumulator element v of a lane holds
+//   MW = 16: row 4 * (lane / 16) + v,                         column lane % 16
+//   MW = 32: row 8 * (v / 4) + 4 * (lane / 32) + v % 4,      column lane % 32
+// of its 16 x 16 (32 x 32) output block.
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+template <int MW>
+struct AccT;
+template <>
+struct AccT<16> { typedef v4f T; static constexpr int N = 4; };
+template <>
+struct AccT<32> { typedef v16f T; static constexpr int N = 16; };
+
+template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT, int MW>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 mxgemm_kernel(GemmArgs p)
 {
     constexpr int NW = WGM * WGN;
     constexpr int NT = NW * 64;
     constexpr int TM = BM / WGM, TN = BN / WGN;
-    constexpr int GA = TM / 16, GB = TN / 16;
-    static_assert(TM % 16 == 0 && TN % 16 == 0, "wave tile must be a multiple of 16");
+    constexpr int GA = TM / MW, GB = TN / MW;
+    static_assert(TM % MW == 0 && TN % MW == 0, "wave tile must be a multiple of the MFMA width");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows come in groups of 8");
+    typedef typename AccT<MW>::T acc_t;
+    constexpr int NACC = AccT<MW>::N;
     constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK;
     // scale bytes: 4 per row and K-step; padded to one 64-lane copy
     constexpr int SA_BYTES = 4 * (BM > 64 ? BM : 64), SB_BYTES = 4 * (BN > 64 ? BN : 64);
@@ -168,14 +188,20 @@ mxgemm_kernel(GemmArgs p)
     constexpr int JA = (IA + NW - 1) / NW, JB = (IB + NW - 1) / NW;
     constexpr int ISA = (BM + 63) / 64, ISB = (BN + 63) / 64;   // scale copies
 
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+    // Two distinct LDS objects (not one array indexed by the step parity):
+    // the compiler then knows a step's copies into one stage never alias
+    // the reads of the other, and does not wait for the copies before the
+    // reads.
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
-    const int l16 = lane & 15, kb = lane >> 4;
+    const int lr = lane & (MW - 1);         // row / column of the lane in a block
+    const int lq = lane / MW;               // lane group
 
     const int steps_per_seg = p.kpr / kBK;
     const int sk = p.kpr >> 5;              // scale bytes per row per segment
@@ -228,15 +254,17 @@ mxgemm_kernel(GemmArgs p)
         const int seg0 = tc.ks * p.segs_per_split;
         const int nsteps = p.segs_per_split * steps_per_seg;
 
-        v4f acc[GA][GB];
+        acc_t acc[GA][GB];
 #pragma unroll
         for (int i = 0; i < GA; ++i)
 #pragma unroll
             for (int j = 0; j < GB; ++j)
-                acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int v = 0; v < NACC; ++v)
+                    acc[i][j][v] = 0.f;
 
-// issue the copies of K-step S into stage buffer BUF
-#define MXG_COPY_STEP(S, BUF)                                                              \
+// issue the copies of K-step S into stage DST
+#define MXG_COPY_STEP(S, DST)                                                              \
     do {                                                                                   \
         const int seg_ = seg0 + (S) / steps_per_seg;                                       \
         const int kk_ = ((S) % steps_per_seg) * kBK;                                       \
@@ -244,7 +272,7 @@ mxgemm_kernel(GemmArgs p)
         const uint8_t* b_ = bt + (int64_t)seg_ * p.kpr + kk_;                               \
         const uint8_t* as_ = p.as + (int64_t)seg_ * p.cms * sk + (kk_ >> 5);                \
         const uint8_t* bs_ = bst + (((int64_t)seg_ * p.kpr + kk_) >> 5);                    \
-        uint8_t* st_ = smem + (BUF) * STAGE;                                               \
+        uint8_t* st_ = (DST);                                                              \
         _Pragma("unroll") for (int j = 0; j < JA; ++j)                                     \
             if (IA % NW == 0 || wave + j * NW < IA)                                        \
                 dma16(a_ + a_off[j], st_ + (wave + j * NW) * 1024);                        \
@@ -262,40 +290,45 @@ mxgemm_kernel(GemmArgs p)
     } while (0)
 
         __syncthreads();   // the previous work item is done with the LDS
-        MXG_COPY_STEP(0, 0);
+        MXG_COPY_STEP(0, stage0);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
-        for (int s = 0; s < nsteps; ++s) {
-            const int buf = s & 1;
+        // One K-step: start the copy of step s + 1 into NXT, multiply the
+        // tiles in CUR, then wait for the copy and synchronise.
+        auto kstep = [&](int s, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
             if (s + 1 < nsteps)
-                MXG_COPY_STEP(s + 1, buf ^ 1);
+                MXG_COPY_STEP(s + 1, nxt);
 
-            const uint8_t* sa_ = smem + buf * STAGE;
+            const uint8_t* sa_ = cur;
             const uint8_t* sb_ = sa_ + A_BYTES;
             const uint8_t* ssa = sb_ + B_BYTES;
             const uint8_t* ssb = ssa + SA_BYTES;
+            // Row r of a fragment group is r = group base + lr with the
+            // group base a multiple of MW >= 16, so r & 7 = lr & 7: a lane's
+            // swizzled byte offsets differ between groups by a constant.
+            const uint8_t* pa = sa_ + (wm * TM + lr) * kBK;
+            const uint8_t* pb = sb_ + (wn * TN + lr) * kBK;
+            const uint8_t* psa = ssa + (wm * TM + lr) * 4;
+            const uint8_t* psb = ssb + (wn * TN + lr) * 4;
+            auto chunk = [&](int c) { return swz(lr, c) * 16; };
 
-            if constexpr (!EXACT) {
-                // Native: one scaled MFMA per (A group, B group) per K-step.
-                // B fragments for the whole step first; A fragments double
-                // buffered so group i + 1 is in flight while group i's MFMAs
-                // run.
-                const int off_lo = l16 * kBK + swz(l16, kb) * 16;
-                const int off_hi = l16 * kBK + swz(l16, kb + 4) * 16;
-                const uint8_t* pa = sa_ + (wm * TM) * kBK;
-                const uint8_t* pb = sb_ + (wn * TN) * kBK;
-                const uint8_t* psa = ssa + (wm * TM + l16) * 4 + kb;
-                const uint8_t* psb = ssb + (wn * TN + l16) * 4 + kb;
+            if constexpr (!EXACT && MW == 16) {
+                // Native, 16 x 16 x 128: one scaled MFMA per (A group, B
+                // group) per K-step.  Lane group q holds K [16q, 16q + 16)
+                // and [64 + 16q, ...); its scale byte is MX block q.  A
+                // fragments double buffered so group i + 1 is in flight
+                // while group i's MFMAs run.
+                const int off_lo = chunk(lq), off_hi = chunk(lq + 4);
                 v8i bf[GB];
                 int sbv[GB];
 #pragma unroll
                 for (int j = 0; j < GB; ++j) {
-                    const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + j * 16 * kBK + off_lo);
-                    const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + j * 16 * kBK + off_hi);
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + j * MW * kBK + off_lo);
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + j * MW * kBK + off_hi);
                     bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    sbv[j] = psb[j * 64];
+                    sbv[j] = psb[j * MW * 4 + lq];
                 }
                 v8i af[2];
                 int sav[2];
@@ -304,17 +337,17 @@ mxgemm_kernel(GemmArgs p)
                     const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + off_hi);
                     af[0] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                    sav[0] = psa[0];
+                    sav[0] = psa[lq];
                 }
 #pragma unroll
                 for (int i = 0; i < GA; ++i) {
                     const int cur = i & 1;
                     if (i + 1 < GA) {
-                        const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + (i + 1) * 16 * kBK + off_lo);
-                        const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + (i + 1) * 16 * kBK + off_hi);
+                        const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + (i + 1) * MW * kBK + off_lo);
+                        const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + (i + 1) * MW * kBK + off_hi);
                         af[cur ^ 1] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                                           (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-                        sav[cur ^ 1] = psa[(i + 1) * 64];
+                        sav[cur ^ 1] = psa[(i + 1) * MW * 4 + lq];
                     }
 #pragma unroll
                     for (int j = 0; j < GB; ++j)
@@ -323,41 +356,80 @@ mxgemm_kernel(GemmArgs p)
                             0, sav[cur], 0, sbv[j]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            } else {
-                // Exact accumulation: each MX block j of the K-step is one
-                // v_mfma_f32_16x16x32_bf16.  Lane group q of a 16-row group
-                // takes 8 codes of block j (K [32j + 8q, 32j + 8q + 8)),
+            } else if constexpr (!EXACT && MW == 32) {
+                // Native, 32 x 32 x 64: two scaled MFMAs (m = 0, 1: K
+                // [64m, 64m + 64)) per (A group, B group) per K-step.  Lane
+                // group h = lane / 32 holds K [64m + 16h, +16) and
+                // [64m + 32 + 16h, +16); its scale byte is MX block 2m + h.
+                v8i bf[GB][2];
+                int sbv[GB][2];
+#pragma unroll
+                for (int j = 0; j < GB; ++j)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m) {
+                        const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + j * MW * kBK + chunk(4 * m + lq));
+                        const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + j * MW * kBK + chunk(4 * m + 2 + lq));
+                        bf[j][m] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        sbv[j][m] = psb[j * MW * 4 + 2 * m + lq];
+                    }
+                v8i af[2][2];
+                int sav[2][2];
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + chunk(4 * m + lq));
+                    const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + chunk(4 * m + 2 + lq));
+                    af[0][m] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                    sav[0][m] = psa[2 * m + lq];
+                }
+#pragma unroll
+                for (int i = 0; i < GA; ++i) {
+                    const int cur = i & 1;
+                    if (i + 1 < GA) {
+#pragma unroll
+                        for (int m = 0; m < 2; ++m) {
+                            const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + (i + 1) * MW * kBK + chunk(4 * m + lq));
+                            const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + (i + 1) * MW * kBK + chunk(4 * m + 2 + lq));
+                            af[cur ^ 1][m] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                                 (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                            sav[cur ^ 1][m] = psa[(i + 1) * MW * 4 + 2 * m + lq];
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < GB; ++j)
+#pragma unroll
+                        for (int m = 0; m < 2; ++m)
+                            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                af[cur][m], bf[j][m], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/,
+                                0, sav[cur][m], 0, sbv[j][m]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else if constexpr (EXACT && MW == 16) {
+                // Exact, 16 x 16 x 32 bf16: each MX block j is one MFMA.
+                // Lane group q takes 8 codes of block j (K [32j + 8q, +8)),
                 // converted to bfloat16 with the block's scale folded in
                 // (exact: 4-bit significands times a power of two).  A and
                 // B use the same K assignment, so every product pairs
-                // correctly; the products are exact in the MFMA and summed
-                // with FP32-grade precision.  Row r of a fragment group is
-                // r = group base + l16 with the group base a multiple of 16,
-                // so r & 7 = l16 & 7 and the swizzled byte offsets of a
-                // lane differ between groups by a constant.
-                //
-                // Per block j: all raw codes of the wave's A and B rows are
-                // read at once, B is converted, then group i + 1 of A is
-                // converted while group i's MFMAs run.
+                // correctly; products are exact in the MFMA and summed with
+                // FP32-grade precision.
                 uint32_t sa_w[GA], sb_w[GB];
 #pragma unroll
                 for (int g = 0; g < GB; ++g)
-                    sb_w[g] = *reinterpret_cast<const uint32_t*>(ssb + (wn * TN + g * 16 + l16) * 4);
+                    sb_w[g] = *reinterpret_cast<const uint32_t*>(psb + g * MW * 4);
 #pragma unroll
                 for (int i = 0; i < GA; ++i)
-                    sa_w[i] = *reinterpret_cast<const uint32_t*>(ssa + (wm * TM + i * 16 + l16) * 4);
+                    sa_w[i] = *reinterpret_cast<const uint32_t*>(psa + i * MW * 4);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int lane_off = l16 * kBK + swz(l16, 2 * j + (kb >> 1)) * 16 + (kb & 1) * 8;
-                    const uint8_t* pa = sa_ + (wm * TM) * kBK + lane_off;
-                    const uint8_t* pb = sb_ + (wn * TN) * kBK + lane_off;
+                    const int lane_off = chunk(2 * j + (lq >> 1)) + (lq & 1) * 8;
                     u32x2 rb[GB], ra[GA];
 #pragma unroll
                     for (int g = 0; g < GB; ++g)
-                        rb[g] = *reinterpret_cast<const u32x2*>(pb + g * 16 * kBK);
+                        rb[g] = *reinterpret_cast<const u32x2*>(pb + g * MW * kBK + lane_off);
 #pragma unroll
                     for (int i = 0; i < GA; ++i)
-                        ra[i] = *reinterpret_cast<const u32x2*>(pa + i * 16 * kBK);
+                        ra[i] = *reinterpret_cast<const u32x2*>(pa + i * MW * kBK + lane_off);
                     v8bf bb[GB];
 #pragma unroll
                     for (int g = 0; g < GB; ++g)
@@ -375,25 +447,87 @@ mxgemm_kernel(GemmArgs p)
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
+            } else {
+                // Exact, 32 x 32 x 16 bf16: MX block j is two MFMAs
+                // (m = 0, 1).  Lane group h = lane / 32 takes K
+                // [32j + 16h + 8m, +8) in MFMA m, so one 16-byte read of
+                // logical chunk 2j + h feeds both.  Codes are converted to
+                // bfloat16 with the block scale folded in (exact), A and B
+                // share the K assignment.
+                uint32_t sa_w[GA], sb_w[GB];
+#pragma unroll
+                for (int g = 0; g < GB; ++g)
+                    sb_w[g] = *reinterpret_cast<const uint32_t*>(psb + g * MW * 4);
+#pragma unroll
+                for (int i = 0; i < GA; ++i)
+                    sa_w[i] = *reinterpret_cast<const uint32_t*>(psa + i * MW * 4);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int off = chunk(2 * j + lq);
+                    u32x4 rb[GB], ra[GA];
+#pragma unroll
+                    for (int g = 0; g < GB; ++g)
+                        rb[g] = *reinterpret_cast<const u32x4*>(pb + g * MW * kBK + off);
+#pragma unroll
+                    for (int i = 0; i < GA; ++i)
+                        ra[i] = *reinterpret_cast<const u32x4*>(pa + i * MW * kBK + off);
+                    v8bf bb[GB][2];
+#pragma unroll
+                    for (int g = 0; g < GB; ++g) {
+                        const float sc = e8m0_to_f32(sb_w[g] >> (8 * j));
+                        bb[g][0] = fp8x8_to_bf16(u32x2{rb[g].x, rb[g].y}, sc);
+                        bb[g][1] = fp8x8_to_bf16(u32x2{rb[g].z, rb[g].w}, sc);
+                    }
+                    v8bf ab[2][2];
+                    {
+                        const float sc = e8m0_to_f32(sa_w[0] >> (8 * j));
+                        ab[0][0] = fp8x8_to_bf16(u32x2{ra[0].x, ra[0].y}, sc);
+                        ab[0][1] = fp8x8_to_bf16(u32x2{ra[0].z, ra[0].w}, sc);
+                    }
+#pragma unroll
+                    for (int i = 0; i < GA; ++i) {
+                        const int cur = i & 1;
+#pragma unroll
+                        for (int g = 0; g < GB; ++g)
+#pragma unroll
+                            for (int m = 0; m < 2; ++m)
+                                acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[cur][m], bb[g][m], acc[i][g], 0, 0, 0);
+                        if (i + 1 < GA) {
+                            const float sc = e8m0_to_f32(sa_w[i + 1] >> (8 * j));
+                            ab[cur ^ 1][0] = fp8x8_to_bf16(u32x2{ra[i + 1].x, ra[i + 1].y}, sc);
+                            ab[cur ^ 1][1] = fp8x8_to_bf16(u32x2{ra[i + 1].z, ra[i + 1].w}, sc);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
             }
 
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+        };
+        for (int s = 0; s < nsteps; s += 2) {
+            kstep(s, stage0, stage1);
+            if (s + 1 < nsteps)
+                kstep(s + 1, stage1, stage0);
         }
 #undef MXG_COPY_STEP
 
         // ---- epilogue --------------------------------------------------
-        const int row_base = m0 + wm * TM + 4 * kb;
-        const int col_base = n0 + wn * TN + l16;
+        // (row, column) in C of accumulator element v of block (i, j)
+        auto out_row = [&](int i, int v) {
+            return MW == 16 ? m0 + wm * TM + i * 16 + 4 * lq + v
+                            : m0 + wm * TM + i * 32 + 8 * (v >> 2) + 4 * lq + (v & 3);
+        };
+        auto out_col = [&](int j) { return n0 + wn * TN + j * MW + lr; };
         if (p.split == 1) {
 #pragma unroll
             for (int i = 0; i < GA; ++i)
 #pragma unroll
                 for (int j = 0; j < GB; ++j) {
-                    const int col = col_base + j * 16;
+                    const int col = out_col(j);
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int row = row_base + i * 16 + v;
+                    for (int v = 0; v < NACC; ++v) {
+                        const int row = out_row(i, v);
                         if (row < p.rows && col < p.N)
                             p.c[(int64_t)row * p.N + col] = f32_to_bf16_rne(acc[i][j][v]);
                     }
@@ -402,13 +536,18 @@ mxgemm_kernel(GemmArgs p)
             // Split-K: every split stores its FP32 partial tile; the last
             // split to arrive sums all partials in split order (so the
             // result does not depend on arrival order) and writes C.
+            constexpr int NQ = NACC / 4;
             const int tile_id = tc.tm * p.tiles_n + tc.tn;
             float* wsp = p.ws + ((int64_t)tile_id * p.split + tc.ks) * (BM * BN);
 #pragma unroll
             for (int i = 0; i < GA; ++i)
 #pragma unroll
                 for (int j = 0; j < GB; ++j)
-                    *reinterpret_cast<v4f*>(wsp + ((i * GB + j) * NT + tid) * 4) = acc[i][j];
+#pragma unroll
+                    for (int q = 0; q < NQ; ++q)
+                        *reinterpret_cast<v4f*>(wsp + (((i * GB + j) * NQ + q) * NT + tid) * 4) =
+                            v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                acc[i][j][4 * q + 3]};
             __threadfence();
             __syncthreads();
             if (tid == 0) {
@@ -423,21 +562,24 @@ mxgemm_kernel(GemmArgs p)
                 for (int i = 0; i < GA; ++i)
 #pragma unroll
                     for (int j = 0; j < GB; ++j) {
-                        v4f sum = *reinterpret_cast<const v4f*>(wst + ((i * GB + j) * NT + tid) * 4);
-                        for (int s = 1; s < p.split; ++s) {
-                            const v4f t = *reinterpret_cast<const v4f*>(
-                                wst + (int64_t)s * (BM * BN) + ((i * GB + j) * NT + tid) * 4);
-                            sum[0] += t[0];
-                            sum[1] += t[1];
-                            sum[2] += t[2];
-                            sum[3] += t[3];
-                        }
-                        const int col = col_base + j * 16;
+                        const int col = out_col(j);
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            const int row = row_base + i * 16 + v;
-                            if (row < p.rows && col < p.N)
-                                p.c[(int64_t)row * p.N + col] = f32_to_bf16_rne(sum[v]);
+                        for (int q = 0; q < NQ; ++q) {
+                            const int64_t off = (((i * GB + j) * NQ + q) * NT + tid) * 4;
+                            v4f sum = *reinterpret_cast<const v4f*>(wst + off);
+                            for (int s = 1; s < p.split; ++s) {
+                                const v4f t = *reinterpret_cast<const v4f*>(wst + (int64_t)s * (BM * BN) + off);
+                                sum[0] += t[0];
+                                sum[1] += t[1];
+                                sum[2] += t[2];
+                                sum[3] += t[3];
+                            }
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const int row = out_row(i, 4 * q + u);
+                                if (row < p.rows && col < p.N)
+                                    p.c[(int64_t)row * p.N + col] = f32_to_bf16_rne(sum[u]);
+                            }
                         }
                     }
                 if (tid == 0)
@@ -447,14 +589,14 @@ mxgemm_kernel(GemmArgs p)
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int OCC>
+template <int BM, int BN, int WGM, int WGN, int OCC, int MW>
 static hipError_t launch_cfg(const GemmArgs& a, int grid, bool exact, hipStream_t stream)
 {
     if (exact)
-        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, true>), dim3(grid),
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, true, MW>), dim3(grid),
                            dim3(WGM * WGN * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, false>), dim3(grid),
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, false, MW>), dim3(grid),
                            dim3(WGM * WGN * 64), 0, stream, a);
     return hipGetLastError();
 }
@@ -462,12 +604,12 @@ static hipError_t launch_cfg(const GemmArgs& a, int grid, bool exact, hipStream_
 hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, int grid, hipStream_t stream)
 {
     switch (cfg) {
-    case 0: return launch_cfg<256, 256, 2, 4, 2>(a, grid, exact, stream);
-    case 1: return launch_cfg<256, 128, 2, 2, 1>(a, grid, exact, stream);
-    case 2: return launch_cfg<128, 128, 2, 2, 1>(a, grid, exact, stream);
-    case 3: return launch_cfg<64, 64, 2, 2, 4>(a, grid, exact, stream);
-    case 4: return launch_cfg<32, 64, 1, 4, 4>(a, grid, exact, stream);
-    case 5: return launch_cfg<16, 64, 1, 4, 4>(a, grid, exact, stream);
+    case 0: return launch_cfg<256, 256, 2, 4, 2, 32>(a, grid, exact, stream);
+    case 1: return launch_cfg<256, 128, 2, 2, 1, 32>(a, grid, exact, stream);
+    case 2: return launch_cfg<128, 128, 2, 2, 1, 32>(a, grid, exact, stream);
+    case 3: return launch_cfg<64, 64, 2, 2, 4, 16>(a, grid, exact, stream);
+    case 4: return launch_cfg<32, 64, 1, 4, 4, 16>(a, grid, exact, stream);
+    case 5: return launch_cfg<16, 64, 1, 4, 4, 16>(a, grid, exact, stream);
     default: return hipErrorInvalidValue;
     }
 }
