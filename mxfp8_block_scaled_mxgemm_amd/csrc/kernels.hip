@@ -125,9 +125,17 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(u32x2 raw, float scale)
 }
 
 // LDS tile rows are kBK = 128 bytes = eight 16-byte chunks.  The chunk
-// position is XOR-swizzled with the row so that the 16 lanes reading the
-// same K chunk of 16 consecutive rows hit different banks.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// position is XOR-swizzled with the row so that lanes reading the same
+// logical chunk of consecutive rows hit different banks.  For 16-row MFMA
+// fragments (MW = 16) row & 7 suffices.  With 32-row fragments the lanes of
+// rows r and r + 16 are served together, so bit 4 of the row flips the
+// chunk as well (measured: 2-way conflicts without it).
+template <int MW>
+__device__ __forceinline__ int swz_t(int row, int chunk)
+{
+    return MW == 32 ? chunk ^ (row & 7) ^ ((row >> 4) & 1) : chunk ^ (row & 7);
+}
+__device__ __forceinline__ int swz(int row, int chunk) { return swz_t<16>(row, chunk); }
 
 // One 16-byte (or 4-byte) piece per lane, straight from global memory into
 // LDS at lds + 16 * lane (resp. 4 * lane); lds must be wave-uniform.
@@ -220,7 +228,7 @@ mxgemm_kernel(GemmArgs p)
         for (int j = 0; j < JA; ++j) {
             const int t = wave + j * NW;                 // copy index
             const int row = 8 * (t < IA ? t : IA - 1) + (lane >> 3);
-            const int ch = (lane & 7) ^ (row & 7);
+            const int ch = swz_t<MW>(row, lane & 7);
             int g = m0 + row;
             g = g < p.rows ? g : p.rows - 1;
             a_off[j] = (uint32_t)((g / p.cms) * p.a_slot_stride) + (uint32_t)((g % p.cms) * p.kpr) + ch * 16;
@@ -229,7 +237,7 @@ mxgemm_kernel(GemmArgs p)
         for (int j = 0; j < JB; ++j) {
             const int t = wave + j * NW;
             const int row = 8 * (t < IB ? t : IB - 1) + (lane >> 3);
-            const int ch = (lane & 7) ^ (row & 7);
+            const int ch = swz_t<MW>(row, lane & 7);
             int g = n0 + row < p.N ? row : p.N - 1 - n0;
             b_off[j] = (uint32_t)g * (uint32_t)p.K + ch * 16;
         }
@@ -311,7 +319,7 @@ mxgemm_kernel(GemmArgs p)
             const uint8_t* pb = sb_ + (wn * TN + lr) * kBK;
             const uint8_t* psa = ssa + (wm * TM + lr) * 4;
             const uint8_t* psb = ssb + (wn * TN + lr) * 4;
-            auto chunk = [&](int c) { return swz(lr, c) * 16; };
+            auto chunk = [&](int c) { return swz_t<MW>(lr, c) * 16; };
 
             if constexpr (!EXACT && MW == 16) {
                 // Native, 16 x 16 x 128: one scaled MFMA per (A group, B
@@ -396,10 +404,12 @@ mxgemm_kernel(GemmArgs p)
                             sav[cur ^ 1][m] = psa[(i + 1) * MW * 4 + 2 * m + lq];
                         }
                     }
+                    // m outer: consecutive MFMAs update different
+                    // accumulators, so none waits for the one before
 #pragma unroll
-                    for (int j = 0; j < GB; ++j)
+                    for (int m = 0; m < 2; ++m)
 #pragma unroll
-                        for (int m = 0; m < 2; ++m)
+                        for (int j = 0; j < GB; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                                 af[cur][m], bf[j][m], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/,
                                 0, sav[cur][m], 0, sbv[j][m]);
@@ -488,9 +498,9 @@ mxgemm_kernel(GemmArgs p)
                     for (int i = 0; i < GA; ++i) {
                         const int cur = i & 1;
 #pragma unroll
-                        for (int g = 0; g < GB; ++g)
+                        for (int m = 0; m < 2; ++m)
 #pragma unroll
-                            for (int m = 0; m < 2; ++m)
+                            for (int g = 0; g < GB; ++g)
                                 acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[cur][m], bb[g][m], acc[i][g], 0, 0, 0);
                         if (i + 1 < GA) {
                             const float sc = e8m0_to_f32(sa_w[i + 1] >> (8 * j));
