@@ -74,15 +74,15 @@ typedef struct mxgemm_seg_plan {
     int32_t split;             /* S: K split over rank-segment groups       */
     int32_t tiles_m, tiles_n;  /* tiles of a full window                    */
     int32_t work_items;        /* tiles_m * tiles_n * S for a full window   */
-    int32_t grid;              /* persistent work-groups per GEMM launch    */
+    int32_t grid;              /* work-groups of a full-window GEMM launch:
+                                  one per work item                        */
     int32_t group_n;           /* N-tiles per zigzag group                  */
     int32_t num_cus;
     int32_t precision;         /* MXGEMM_PRECISION_*                        */
     int32_t reserved;
     int64_t slot_bytes;        /* one staging buffer: R*commMSize*kPerRank  */
     int64_t scale_slot_bytes;  /* its scales: R*commMSize*kPerRank/32       */
-    int64_t workspace_bytes;   /* FP32 split-K partials                     */
-    int64_t counter_count;     /* split-K arrival counters                  */
+    int64_t workspace_bytes;   /* FP32 split-K partials: S * W * commMSize * N * 4 */
 } mxgemm_seg_plan_t;
 
 /* Optional knobs for mxgemm_seg_create_ex / mxgemm_seg_plan; -1 = automatic. */
@@ -90,7 +90,6 @@ typedef struct mxgemm_seg_options {
     int32_t tile_cfg;          /* force a tile configuration (table index)  */
     int32_t split;             /* force S (must divide rank_size)           */
     int32_t chunks_per_window; /* force W (must divide buffer_count)        */
-    int32_t grid;              /* cap the persistent grid                   */
     int32_t precision;         /* MXGEMM_PRECISION_* (-1 = EXACT)           */
 } mxgemm_seg_options_t;
 
@@ -109,7 +108,7 @@ typedef struct mxgemm_seg_options {
  * 32; this build also needs kPerRank % 128 == 0 (one MFMA K-step), else
  * MXGEMM_EUNSUPPORTED.  Allocates, on the current device, the staging ring
  * (buffer_count * R * commMSize * kPerRank * 33/32 bytes), the split-K
- * workspace and counters, a side stream at default priority and the ring's
+ * workspace, a side stream at default priority and the ring's
  * events; run() allocates nothing.  Errors: EINVAL, ENOMEM, EHIP,
  * EUNSUPPORTED (device is not gfx950).  *out is set only on success.
  */
@@ -138,7 +137,10 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
  * side stream into ring slot j % buffer_count; the GEMM for a chunk starts
  * only after its copy (ready event) and a slot is refilled only after the
  * GEMM that read it (credit event) -- the ready/credit pairing of
- * MatmulProcess / AllToAllProcess.  The side stream forks from and joins
+ * MatmulProcess / AllToAllProcess.  With S > 1 a window's GEMM writes FP32
+ * partials into the handle's workspace and a second kernel on `stream` sums
+ * them in split order into C (the result does not depend on timing).  The
+ * side stream forks from and joins
  * back into `stream`, so work before and after run() on `stream` stays
  * ordered and the call can be captured into a HIP graph.  A handle must not
  * be run concurrently on two streams; distinct handles may.
@@ -164,12 +166,13 @@ int mxgemm_seg_plan(mxgemm_seg_plan_t* out, int64_t M, int64_t kPerRank, int32_t
                     int64_t N, int64_t commMSize, int32_t buffer_count, int32_t num_cus,
                     const mxgemm_seg_options_t* opts);
 
-/* Decode persistent work item `w` of a window with `rows` rows under `plan`
- * into (tile row, tile column, K-split index), exactly as the GEMM kernel
- * does (flattened work ID with zigzag N-groups; Triton-distributed-Ascend
+/* Decode work item `w` of a window with `rows` rows under `plan` into
+ * (tile row, tile column, K-split index), exactly as the GEMM kernel does
+ * (flattened work ID with zigzag N-groups; Triton-distributed-Ascend
  * performance guide, section 1.2 on flattening the work ID and section 1.4
- * on the zigzag swizzle).  Also returns the logical work ID the kernel's
- * work-group `block` starts from (XCD-aware remap).  Host only.
+ * on the zigzag swizzle).  Also returns the work item that work-group
+ * `block` of that window's launch (one work-group per work item) takes
+ * under the XCD-aware remap.  Host only.
  * Errors: EINVAL (w or block out of range). */
 int mxgemm_seg_decode(const mxgemm_seg_plan_t* plan, int64_t rows, int32_t w, int32_t block,
                       int32_t* tile_m_idx, int32_t* tile_n_idx, int32_t* split_idx,

@@ -46,7 +46,7 @@ class Plan(ctypes.Structure):
         ("work_items", ctypes.c_int32), ("grid", ctypes.c_int32), ("group_n", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("precision", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("slot_bytes", ctypes.c_int64), ("scale_slot_bytes", ctypes.c_int64),
-        ("workspace_bytes", ctypes.c_int64), ("counter_count", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
     def as_dict(self):
@@ -59,12 +59,12 @@ PRECISION_NATIVE = 1
 
 class Options(ctypes.Structure):
     _fields_ = [("tile_cfg", ctypes.c_int32), ("split", ctypes.c_int32),
-                ("chunks_per_window", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("chunks_per_window", ctypes.c_int32),
                 ("precision", ctypes.c_int32)]
 
 
-def options(tile_cfg=-1, split=-1, chunks_per_window=-1, grid=-1, precision=-1) -> Options:
-    return Options(tile_cfg, split, chunks_per_window, grid, precision)
+def options(tile_cfg=-1, split=-1, chunks_per_window=-1, precision=-1) -> Options:
+    return Options(tile_cfg, split, chunks_per_window, precision)
 
 
 _lib = None

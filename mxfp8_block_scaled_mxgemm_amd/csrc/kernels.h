@@ -39,10 +39,18 @@ struct GemmArgs {
     const uint8_t* b;         // [N][K]
     const uint8_t* bs;        // [N][K/32]
     uint16_t* c;              // C + first window row * N
-    float* ws;                // split-K partials
-    int* counters;            // split-K arrival counters (zero between launches)
+    float* ws;                // split-K partials [split][rows][N] (split > 1)
     int rows, N, K, kpr, cms;
     int tiles_m, tiles_n, split, segs_per_split, group_n, total_work;
+    int c_vec4;               // C rows may be written 4 elements (8 bytes) at a time
+};
+
+// Split-K reduction: c[r][n] = bf16(sum over s in order of ws[s][r][n]).
+struct ReduceArgs {
+    const float* ws;
+    uint16_t* c;
+    int rows, N, split;
+    int c_vec4;
 };
 
 struct QuantArgs {
@@ -53,7 +61,9 @@ struct QuantArgs {
 };
 
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
-hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, int grid, hipStream_t stream);
+// One work-group per work item (a.total_work of them).
+hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 
 }  // namespace mxg

@@ -92,17 +92,18 @@ hipError_t launch_stage(const StageArgs& a, hipStream_t stream)
 
 // ------------------------------------------------------------------ GEMM --
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two floats -> bfloat16, round to nearest even (v_cvt_pk_bf16_f32), `lo`
+// in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u)
-        return 0x7FC0;
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{lo, hi}, v2bf));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)pack_bf16x2(f, 0.f); }
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // E8M0 scale byte -> 2^(s - 127) as float, branch-free: v_ldexp_f32 gives
@@ -150,23 +151,22 @@ __device__ __forceinline__ void dma4(const void* g, void* lds)
 
 // Block-scaled GEMM over one window of staged rows.
 //
-// Work-group tile BM x BN, WGM x WGN waves, K-step 128 (four MX blocks).
-// Each K-step's A and B tiles and their scale bytes are copied global ->
-// LDS by the load unit itself (global_load_lds), double-buffered, so the
-// next step's copy runs while the current one is multiplied and no
-// registers hold staged data.  A lane of a copy instruction writes 16 bytes
-// at lds_base + 16 * lane: eight lanes fill one 128-byte tile row, and lane
-// L fetches the logical chunk that the row's XOR swizzle places at physical
-// chunk L % 8.
+// Work-group tile BM x BN, K-step 128 (four MX blocks).  Each K-step's A and
+// B tiles and their scale bytes are copied global -> LDS by the load unit
+// itself (global_load_lds), double-buffered, so the next step's copy runs
+// while the current one is multiplied and no registers hold staged data.
+// A lane of a copy instruction writes 16 bytes at lds_base + 16 * lane:
+// eight lanes fill one 128-byte tile row, and lane L fetches the logical
+// chunk that the row's XOR swizzle places at physical chunk L % 8.
 //
-// MW is the MFMA width.  MW = 16: v_mfma_scale_f32_16x16x128_f8f6f4
-// (native) or v_mfma_f32_16x16x32_bf16 (exact).  MW = 32:
-// v_mfma_scale_f32_32x32x64_f8f6f4 (native) or v_mfma_f32_32x32x16_bf16
-// (exact); every 16-byte LDS read then feeds whole instructions.
-// Accumulator element v of a lane holds
-//   MW = 16: row 4 * (lane / 16) + v,                         column lane % 16
-//   MW = 32: row 8 * (v / 4) + 4 * (lane / 32) + v % 4,      column lane % 32
-// of its 16 x 16 (32 x 32) output block.
+// MFMA forms and accumulator layouts (MW = MFMA width):
+//   MW = 16: v_mfma_scale_f32_16x16x128_f8f6f4 (native) or
+//            v_mfma_f32_16x16x32_bf16 (exact); element v of a lane holds
+//            row 4 * (lane / 16) + v, column lane % 16;
+//   MW = 32: v_mfma_scale_f32_32x32x64_f8f6f4 (native) or
+//            v_mfma_f32_32x32x16_bf16 (exact); element v holds row
+//            8 * (v / 4) + 4 * (lane / 32) + v % 4, column lane % 32
+// of its MW x MW output block.
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 template <int MW>
@@ -176,91 +176,265 @@ struct AccT<16> { typedef v4f T; static constexpr int N = 4; };
 template <>
 struct AccT<32> { typedef v16f T; static constexpr int N = 16; };
 
+// LDS stage layout of a BM x BN tile pair: A rows, B rows (128 bytes each),
+// then 4 scale bytes per A row and per B row (padded to one 64-lane copy).
+template <int BM, int BN, int NW>
+struct StageGeom {
+    static constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK;
+    static constexpr int SA_BYTES = 4 * (BM > 64 ? BM : 64), SB_BYTES = 4 * (BN > 64 ? BN : 64);
+    static constexpr int SA_OFF = A_BYTES + B_BYTES, SB_OFF = SA_OFF + SA_BYTES;
+    static constexpr int STAGE = SB_OFF + SB_BYTES;
+    static constexpr int IA = BM / 8, IB = BN / 8;                  // 1 KB copies per K-step
+    static constexpr int JA = (IA + NW - 1) / NW, JB = (IB + NW - 1) / NW;
+    static constexpr int ISA = (BM + 63) / 64, ISB = (BN + 63) / 64; // 256-byte scale copies
+    static constexpr int KSA = (ISA + NW - 1) / NW, KSB = (ISB + NW - 1) / NW;
+};
+
+// The copies of one work item: per-lane 32-bit source offsets, fixed for
+// the item.  A offsets are relative to the window's ring base (the ring is
+// < 2 GiB), B offsets relative to row n0 of B.  Rows past the edge are
+// clamped to the last valid row; their results are never stored.
+template <int BM, int BN, int NW, int MW>
+struct CopyOffsets {
+    typedef StageGeom<BM, BN, NW> G;
+    uint32_t a[G::JA], b[G::JB], as[G::KSA], bs[G::KSB];
+};
+
+template <int BM, int BN, int NW, int MW>
+__device__ __forceinline__ void copy_offsets(const GemmArgs& p, int m0, int n0, int wave, int lane,
+                                             CopyOffsets<BM, BN, NW, MW>& o)
+{
+    typedef StageGeom<BM, BN, NW> G;
+    const int sk = p.kpr >> 5;
+    const int K32 = p.K >> 5;
+#pragma unroll
+    for (int j = 0; j < G::JA; ++j) {
+        const int t = wave + j * NW;
+        const int row = 8 * (t < G::IA ? t : G::IA - 1) + (lane >> 3);
+        const int ch = swz_t<MW>(row, lane & 7);
+        int g = m0 + row;
+        g = g < p.rows ? g : p.rows - 1;
+        o.a[j] = (uint32_t)((g / p.cms) * p.a_slot_stride) + (uint32_t)((g % p.cms) * p.kpr) + ch * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < G::JB; ++j) {
+        const int t = wave + j * NW;
+        const int row = 8 * (t < G::IB ? t : G::IB - 1) + (lane >> 3);
+        const int ch = swz_t<MW>(row, lane & 7);
+        const int g = n0 + row < p.N ? row : p.N - 1 - n0;
+        o.b[j] = (uint32_t)g * (uint32_t)p.K + ch * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < G::KSA; ++j) {
+        const int t = wave + j * NW;
+        int row = 64 * (t < G::ISA ? t : G::ISA - 1) + lane;
+        row = row < BM ? row : BM - 1;
+        int g = m0 + row;
+        g = g < p.rows ? g : p.rows - 1;
+        o.as[j] = (uint32_t)((g / p.cms) * p.as_slot_stride) + (uint32_t)((g % p.cms) * sk);
+    }
+#pragma unroll
+    for (int j = 0; j < G::KSB; ++j) {
+        const int t = wave + j * NW;
+        int row = 64 * (t < G::ISB ? t : G::ISB - 1) + lane;
+        row = row < BN ? row : BN - 1;
+        const int g = n0 + row < p.N ? row : p.N - 1 - n0;
+        o.bs[j] = (uint32_t)g * (uint32_t)K32;
+    }
+}
+
+// Global addresses of K-step s of a work item whose first segment is seg0
+// and whose B tile starts at row n0 (all wave-uniform).
+struct StepSrc {
+    const uint8_t* a;
+    const uint8_t* b;
+    const uint8_t* as;
+    const uint8_t* bs;
+};
+
+__device__ __forceinline__ StepSrc step_src(const GemmArgs& p, int seg0, int n0, int s)
+{
+    const int steps_per_seg = p.kpr / kBK;
+    const int sk = p.kpr >> 5;
+    const int seg = seg0 + s / steps_per_seg;
+    const int kk = (s % steps_per_seg) * kBK;
+    StepSrc r;
+    r.a = p.a + (int64_t)seg * p.cms * p.kpr + kk;
+    r.b = p.b + (int64_t)n0 * p.K + (int64_t)seg * p.kpr + kk;
+    r.as = p.as + (int64_t)seg * p.cms * sk + (kk >> 5);
+    r.bs = p.bs + (((int64_t)n0 * p.K + (int64_t)seg * p.kpr + kk) >> 5);
+    return r;
+}
+
+// Issue the copies of one K-step (sources `src`) into the stage at dst.
+// With nparts > 1 only share `part` of them (copies j with
+// j % nparts == part), so the issue can be spread between other work.
+template <int BM, int BN, int NW, int MW>
+__device__ __forceinline__ void copy_issue(const CopyOffsets<BM, BN, NW, MW>& o, const StepSrc& src, uint8_t* dst,
+                                           int wave, int part = 0, int nparts = 1)
+{
+    typedef StageGeom<BM, BN, NW> G;
+#pragma unroll
+    for (int j = 0; j < G::JA; ++j)
+        if (j % nparts == part && (G::IA % NW == 0 || wave + j * NW < G::IA))
+            dma16(src.a + o.a[j], dst + (wave + j * NW) * 1024);
+#pragma unroll
+    for (int j = 0; j < G::JB; ++j)
+        if (j % nparts == part && (G::IB % NW == 0 || wave + j * NW < G::IB))
+            dma16(src.b + o.b[j], dst + G::A_BYTES + (wave + j * NW) * 1024);
+#pragma unroll
+    for (int j = 0; j < G::KSA; ++j)
+        if (j % nparts == part && (G::ISA % NW == 0 || wave + j * NW < G::ISA))
+            dma4(src.as + o.as[j], dst + G::SA_OFF + (wave + j * NW) * 256);
+#pragma unroll
+    for (int j = 0; j < G::KSB; ++j)
+        if ((j + 1) % nparts == part && (G::ISB % NW == 0 || wave + j * NW < G::ISB))
+            dma4(src.bs + o.bs[j], dst + G::SB_OFF + (wave + j * NW) * 256);
+}
+
+// Write a wave's accumulators: GA x GB blocks of MW x MW, block (i, j)
+// covering rows row0 + MW i and columns col0 + MW j of C.  Every MFMA takes
+// the B fragment as its first operand (it computes the transposed block),
+// so element v of a lane holds row lane % MW and column
+//   MW = 32: 8 (v / 4) + 4 (lane / 32) + v % 4,
+//   MW = 16: 4 (lane / 16) + v:
+// four consecutive columns per v / 4, written as one 8-byte (C) or 16-byte
+// (split-K partial) store where the layout allows.  With split > 1 the
+// FP32 partial goes to ws[split index][row][column] and a second kernel
+// sums the splits.
+template <int GA, int GB, int MW, typename acc_t>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoord& tc, acc_t (&acc)[GA][GB],
+                                           int row0, int col0, int lane)
+{
+    constexpr int NQ = AccT<MW>::N / 4;
+    const int lr = lane & (MW - 1), lq = lane / MW;
+    // The lane's first element.  Hidden from the optimiser: otherwise the
+    // lane-dependent parts of every store address are computed up front
+    // and held in registers across the K loop.
+    int64_t lane_base = (int64_t)(row0 + lr) * p.N + col0 + 4 * lq;
+    asm volatile("" : "+v"(lane_base));
+    const bool partial = p.split > 1;
+    const bool vec = partial ? (p.N & 3) == 0 : p.c_vec4 != 0;
+    float* wsp = p.ws + (int64_t)tc.ks * p.rows * p.N;
+#pragma unroll
+    for (int i = 0; i < GA; ++i) {
+        if (row0 + i * MW + lr >= p.rows)
+            continue;
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const int cofs = j * MW + (MW == 32 ? 8 * q : 0);
+                const int col = col0 + 4 * lq + cofs;
+                const int64_t off = lane_base + (int64_t)(i * MW) * p.N + cofs;
+                const v4f x = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                if (vec && col + 3 < p.N) {
+                    if (partial)
+                        *reinterpret_cast<v4f*>(wsp + off) = x;
+                    else
+                        *reinterpret_cast<u32x2*>(p.c + off) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (col + u < p.N) {
+                            if (partial)
+                                wsp[off + u] = x[u];
+                            else
+                                p.c[off + u] = f32_to_bf16_rne(x[u]);
+                        }
+                }
+            }
+    }
+}
+
+// Split-K reduction: four consecutive outputs per thread; the splits are
+// summed in index order, so the result does not depend on timing.
+__global__ void __launch_bounds__(256) reduce_kernel(ReduceArgs p)
+{
+    const int64_t total = (int64_t)p.rows * p.N;
+    const int64_t slice = total;
+    const int64_t i4 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i4 >= total)
+        return;
+    if ((p.N & 3) == 0) {
+        v4f s = *reinterpret_cast<const v4f*>(p.ws + i4);
+        for (int k = 1; k < p.split; ++k) {
+            const v4f t = *reinterpret_cast<const v4f*>(p.ws + (int64_t)k * slice + i4);
+            s[0] += t[0];
+            s[1] += t[1];
+            s[2] += t[2];
+            s[3] += t[3];
+        }
+        if (p.c_vec4) {
+            *reinterpret_cast<u32x2*>(p.c + i4) = u32x2{pack_bf16x2(s[0], s[1]), pack_bf16x2(s[2], s[3])};
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                p.c[i4 + u] = f32_to_bf16_rne(s[u]);
+        }
+        return;
+    }
+    for (int64_t e = i4; e < i4 + 4 && e < total; ++e) {
+        float s = p.ws[e];
+        for (int k = 1; k < p.split; ++k)
+            s += p.ws[(int64_t)k * slice + e];
+        p.c[e] = f32_to_bf16_rne(s);
+    }
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream)
+{
+    const int64_t threads = ((int64_t)a.rows * a.N + 3) / 4;
+    const int64_t blocks = (threads + 255) / 256;
+    if (blocks == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+// Block-scaled GEMM, scaled-MFMA (native) forms and the 16-wide exact form.
+// WGM x WGN waves of (BM / WGM) x (BN / WGN).
 template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT, int MW>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 mxgemm_kernel(GemmArgs p)
 {
     constexpr int NW = WGM * WGN;
-    constexpr int NT = NW * 64;
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int GA = TM / MW, GB = TN / MW;
     static_assert(TM % MW == 0 && TN % MW == 0, "wave tile must be a multiple of the MFMA width");
     static_assert(BM % 8 == 0 && BN % 8 == 0, "tile rows come in groups of 8");
+    static_assert(!(EXACT && MW == 32), "the 32-wide exact form is mxgemm_exact_kernel");
     typedef typename AccT<MW>::T acc_t;
     constexpr int NACC = AccT<MW>::N;
-    constexpr int A_BYTES = BM * kBK, B_BYTES = BN * kBK;
-    // scale bytes: 4 per row and K-step; padded to one 64-lane copy
-    constexpr int SA_BYTES = 4 * (BM > 64 ? BM : 64), SB_BYTES = 4 * (BN > 64 ? BN : 64);
-    constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
-    constexpr int IA = BM / 8, IB = BN / 8;            // 1 KB copies per K-step
-    constexpr int JA = (IA + NW - 1) / NW, JB = (IB + NW - 1) / NW;
-    constexpr int ISA = (BM + 63) / 64, ISB = (BN + 63) / 64;   // scale copies
+    typedef StageGeom<BM, BN, NW> G;
 
     // Two distinct LDS objects (not one array indexed by the step parity):
     // the compiler then knows a step's copies into one stage never alias
     // the reads of the other, and does not wait for the copies before the
     // reads.
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[STAGE];
-    __shared__ int s_last;
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[G::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
     const int wm = wave / WGN, wn = wave % WGN;
     const int lr = lane & (MW - 1);         // row / column of the lane in a block
     const int lq = lane / MW;               // lane group
 
-    const int steps_per_seg = p.kpr / kBK;
-    const int sk = p.kpr >> 5;              // scale bytes per row per segment
-    const int K32 = p.K >> 5;
-
-    for (int w = remap_block(blockIdx.x, gridDim.x); w < p.total_work; w += gridDim.x) {
+    // one work item per work-group (the dispatcher does the load balancing;
+    // a persistent loop would hold the epilogue's per-lane address terms in
+    // registers across the K loop)
+    const int w = remap_block(blockIdx.x, gridDim.x);
+    if (w >= p.total_work)
+        return;
+    {
         const TileCoord tc = decode_work(w, p.tiles_m, p.tiles_n, p.split, p.group_n);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
-
-        // Per-lane 32-bit source offsets of this wave's copies.  A offsets
-        // are relative to the window's ring base (the ring is < 2 GiB), B
-        // offsets relative to row n0 of B.  Rows past the edge are clamped
-        // to the last valid row; their results are never stored.
-        uint32_t a_off[JA], b_off[JB], as_off[ISA], bs_off[ISB];
-#pragma unroll
-        for (int j = 0; j < JA; ++j) {
-            const int t = wave + j * NW;                 // copy index
-            const int row = 8 * (t < IA ? t : IA - 1) + (lane >> 3);
-            const int ch = swz_t<MW>(row, lane & 7);
-            int g = m0 + row;
-            g = g < p.rows ? g : p.rows - 1;
-            a_off[j] = (uint32_t)((g / p.cms) * p.a_slot_stride) + (uint32_t)((g % p.cms) * p.kpr) + ch * 16;
-        }
-#pragma unroll
-        for (int j = 0; j < JB; ++j) {
-            const int t = wave + j * NW;
-            const int row = 8 * (t < IB ? t : IB - 1) + (lane >> 3);
-            const int ch = swz_t<MW>(row, lane & 7);
-            int g = n0 + row < p.N ? row : p.N - 1 - n0;
-            b_off[j] = (uint32_t)g * (uint32_t)p.K + ch * 16;
-        }
-#pragma unroll
-        for (int j = 0; j < ISA; ++j) {
-            int row = 64 * j + lane;
-            row = row < BM ? row : BM - 1;
-            int g = m0 + row;
-            g = g < p.rows ? g : p.rows - 1;
-            as_off[j] = (uint32_t)((g / p.cms) * p.as_slot_stride) + (uint32_t)((g % p.cms) * sk);
-        }
-#pragma unroll
-        for (int j = 0; j < ISB; ++j) {
-            int row = 64 * j + lane;
-            row = row < BN ? row : BN - 1;
-            int g = n0 + row < p.N ? row : p.N - 1 - n0;
-            bs_off[j] = (uint32_t)g * (uint32_t)K32;
-        }
-        const uint8_t* __restrict__ bt = p.b + (int64_t)n0 * p.K;
-        const uint8_t* __restrict__ bst = p.bs + (int64_t)n0 * K32;
-
+        CopyOffsets<BM, BN, NW, MW> co;
+        copy_offsets(p, m0, n0, wave, lane, co);
         const int seg0 = tc.ks * p.segs_per_split;
-        const int nsteps = p.segs_per_split * steps_per_seg;
+        const int nsteps = p.segs_per_split * (p.kpr / kBK);
 
         acc_t acc[GA][GB];
 #pragma unroll
@@ -271,34 +445,7 @@ mxgemm_kernel(GemmArgs p)
                 for (int v = 0; v < NACC; ++v)
                     acc[i][j][v] = 0.f;
 
-// issue the copies of K-step S into stage DST
-#define MXG_COPY_STEP(S, DST)                                                              \
-    do {                                                                                   \
-        const int seg_ = seg0 + (S) / steps_per_seg;                                       \
-        const int kk_ = ((S) % steps_per_seg) * kBK;                                       \
-        const uint8_t* a_ = p.a + (int64_t)seg_ * p.cms * p.kpr + kk_;                      \
-        const uint8_t* b_ = bt + (int64_t)seg_ * p.kpr + kk_;                               \
-        const uint8_t* as_ = p.as + (int64_t)seg_ * p.cms * sk + (kk_ >> 5);                \
-        const uint8_t* bs_ = bst + (((int64_t)seg_ * p.kpr + kk_) >> 5);                    \
-        uint8_t* st_ = (DST);                                                              \
-        _Pragma("unroll") for (int j = 0; j < JA; ++j)                                     \
-            if (IA % NW == 0 || wave + j * NW < IA)                                        \
-                dma16(a_ + a_off[j], st_ + (wave + j * NW) * 1024);                        \
-        _Pragma("unroll") for (int j = 0; j < JB; ++j)                                     \
-            if (IB % NW == 0 || wave + j * NW < IB)                                        \
-                dma16(b_ + b_off[j], st_ + A_BYTES + (wave + j * NW) * 1024);              \
-        if (wave == 0) {                                                                   \
-            _Pragma("unroll") for (int j = 0; j < ISA; ++j)                                \
-                dma4(as_ + as_off[j], st_ + A_BYTES + B_BYTES + j * 256);                  \
-        }                                                                                  \
-        if (wave == NW - 1) {                                                              \
-            _Pragma("unroll") for (int j = 0; j < ISB; ++j)                                \
-                dma4(bs_ + bs_off[j], st_ + A_BYTES + B_BYTES + SA_BYTES + j * 256);       \
-        }                                                                                  \
-    } while (0)
-
-        __syncthreads();   // the previous work item is done with the LDS
-        MXG_COPY_STEP(0, stage0);
+        copy_issue(co, step_src(p, seg0, n0, 0), stage0, wave);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
@@ -306,19 +453,16 @@ mxgemm_kernel(GemmArgs p)
         // tiles in CUR, then wait for the copy and synchronise.
         auto kstep = [&](int s, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
             if (s + 1 < nsteps)
-                MXG_COPY_STEP(s + 1, nxt);
+                copy_issue(co, step_src(p, seg0, n0, s + 1), nxt, wave);
 
-            const uint8_t* sa_ = cur;
-            const uint8_t* sb_ = sa_ + A_BYTES;
-            const uint8_t* ssa = sb_ + B_BYTES;
-            const uint8_t* ssb = ssa + SA_BYTES;
             // Row r of a fragment group is r = group base + lr with the
-            // group base a multiple of MW >= 16, so r & 7 = lr & 7: a lane's
-            // swizzled byte offsets differ between groups by a constant.
-            const uint8_t* pa = sa_ + (wm * TM + lr) * kBK;
-            const uint8_t* pb = sb_ + (wn * TN + lr) * kBK;
-            const uint8_t* psa = ssa + (wm * TM + lr) * 4;
-            const uint8_t* psb = ssb + (wn * TN + lr) * 4;
+            // group base a multiple of MW >= 16, so the swizzle key of r
+            // equals that of lr: a lane's swizzled byte offsets differ
+            // between groups by a constant.
+            const uint8_t* pa = cur + (wm * TM + lr) * kBK;
+            const uint8_t* pb = cur + G::A_BYTES + (wn * TN + lr) * kBK;
+            const uint8_t* psa = cur + G::SA_OFF + (wm * TM + lr) * 4;
+            const uint8_t* psb = cur + G::SB_OFF + (wn * TN + lr) * 4;
             auto chunk = [&](int c) { return swz_t<MW>(lr, c) * 16; };
 
             if constexpr (!EXACT && MW == 16) {
@@ -360,8 +504,8 @@ mxgemm_kernel(GemmArgs p)
 #pragma unroll
                     for (int j = 0; j < GB; ++j)
                         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            af[cur], bf[j], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/,
-                            0, sav[cur], 0, sbv[j]);
+                            bf[j], af[cur], acc[i][j], 0 /*E4M3*/, 0 /*E4M3*/,
+                            0, sbv[j], 0, sav[cur]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else if constexpr (!EXACT && MW == 32) {
@@ -411,11 +555,11 @@ mxgemm_kernel(GemmArgs p)
 #pragma unroll
                         for (int j = 0; j < GB; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                af[cur][m], bf[j][m], acc[i][j], 0 /*A: E4M3*/, 0 /*B: E4M3*/,
-                                0, sav[cur][m], 0, sbv[j][m]);
+                                bf[j][m], af[cur][m], acc[i][j], 0 /*E4M3*/, 0 /*E4M3*/,
+                                0, sbv[j][m], 0, sav[cur][m]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
-            } else if constexpr (EXACT && MW == 16) {
+            } else {
                 // Exact, 16 x 16 x 32 bf16: each MX block j is one MFMA.
                 // Lane group q takes 8 codes of block j (K [32j + 8q, +8)),
                 // converted to bfloat16 with the block's scale folded in
@@ -451,62 +595,9 @@ mxgemm_kernel(GemmArgs p)
                         const int cur = i & 1;
 #pragma unroll
                         for (int g = 0; g < GB; ++g)
-                            acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab[cur], bb[g], acc[i][g], 0, 0, 0);
+                            acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[g], ab[cur], acc[i][g], 0, 0, 0);
                         if (i + 1 < GA)
                             ab[cur ^ 1] = fp8x8_to_bf16(ra[i + 1], e8m0_to_f32(sa_w[i + 1] >> (8 * j)));
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-            } else {
-                // Exact, 32 x 32 x 16 bf16: MX block j is two MFMAs
-                // (m = 0, 1).  Lane group h = lane / 32 takes K
-                // [32j + 16h + 8m, +8) in MFMA m, so one 16-byte read of
-                // logical chunk 2j + h feeds both.  Codes are converted to
-                // bfloat16 with the block scale folded in (exact), A and B
-                // share the K assignment.
-                uint32_t sa_w[GA], sb_w[GB];
-#pragma unroll
-                for (int g = 0; g < GB; ++g)
-                    sb_w[g] = *reinterpret_cast<const uint32_t*>(psb + g * MW * 4);
-#pragma unroll
-                for (int i = 0; i < GA; ++i)
-                    sa_w[i] = *reinterpret_cast<const uint32_t*>(psa + i * MW * 4);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int off = chunk(2 * j + lq);
-                    u32x4 rb[GB], ra[GA];
-#pragma unroll
-                    for (int g = 0; g < GB; ++g)
-                        rb[g] = *reinterpret_cast<const u32x4*>(pb + g * MW * kBK + off);
-#pragma unroll
-                    for (int i = 0; i < GA; ++i)
-                        ra[i] = *reinterpret_cast<const u32x4*>(pa + i * MW * kBK + off);
-                    v8bf bb[GB][2];
-#pragma unroll
-                    for (int g = 0; g < GB; ++g) {
-                        const float sc = e8m0_to_f32(sb_w[g] >> (8 * j));
-                        bb[g][0] = fp8x8_to_bf16(u32x2{rb[g].x, rb[g].y}, sc);
-                        bb[g][1] = fp8x8_to_bf16(u32x2{rb[g].z, rb[g].w}, sc);
-                    }
-                    v8bf ab[2][2];
-                    {
-                        const float sc = e8m0_to_f32(sa_w[0] >> (8 * j));
-                        ab[0][0] = fp8x8_to_bf16(u32x2{ra[0].x, ra[0].y}, sc);
-                        ab[0][1] = fp8x8_to_bf16(u32x2{ra[0].z, ra[0].w}, sc);
-                    }
-#pragma unroll
-                    for (int i = 0; i < GA; ++i) {
-                        const int cur = i & 1;
-#pragma unroll
-                        for (int m = 0; m < 2; ++m)
-#pragma unroll
-                            for (int g = 0; g < GB; ++g)
-                                acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[cur][m], bb[g][m], acc[i][g], 0, 0, 0);
-                        if (i + 1 < GA) {
-                            const float sc = e8m0_to_f32(sa_w[i + 1] >> (8 * j));
-                            ab[cur ^ 1][0] = fp8x8_to_bf16(u32x2{ra[i + 1].x, ra[i + 1].y}, sc);
-                            ab[cur ^ 1][1] = fp8x8_to_bf16(u32x2{ra[i + 1].z, ra[i + 1].w}, sc);
-                        }
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
@@ -520,109 +611,310 @@ mxgemm_kernel(GemmArgs p)
             if (s + 1 < nsteps)
                 kstep(s + 1, stage1, stage0);
         }
-#undef MXG_COPY_STEP
 
-        // ---- epilogue --------------------------------------------------
-        // (row, column) in C of accumulator element v of block (i, j)
-        auto out_row = [&](int i, int v) {
-            return MW == 16 ? m0 + wm * TM + i * 16 + 4 * lq + v
-                            : m0 + wm * TM + i * 32 + 8 * (v >> 2) + 4 * lq + (v & 3);
-        };
-        auto out_col = [&](int j) { return n0 + wn * TN + j * MW + lr; };
-        if (p.split == 1) {
+        store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
+    }
+}
+
+// Eight E4M3 codes of one MX block row piece (16 bytes = two MFMA operands)
+// -> bfloat16 operands with the block's scale byte j of `sw` folded in.
+__device__ __forceinline__ void convert_codes(const u32x4& r, uint32_t sw, int j, v8bf (&cv)[2])
+{
+    const float sc = e8m0_to_f32(sw >> (8 * j));
+    cv[0] = fp8x8_to_bf16(u32x2{r.x, r.y}, sc);
+    cv[1] = fp8x8_to_bf16(u32x2{r.z, r.w}, sc);
+}
+
+// Word e (0..7) of the bfloat16 operands of one 16-byte code piece: codes
+// 2e, 2e + 1 (bytes of r in order) times sc.
+__device__ __forceinline__ uint32_t cvt_word(const u32x4& r, float sc, int e)
+{
+    const uint32_t src = e < 2 ? r.x : e < 4 ? r.y : e < 6 ? r.z : r.w;
+    return (e & 1) ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, true))
+                   : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, sc, false));
+}
+
+// Number of copies copy_issue(..., part, nparts) issues at most, and the
+// t-th of them alone (same order), so the issue can be interleaved.
+template <int BM, int BN, int NW, int MW>
+__device__ __forceinline__ void copy_one(const CopyOffsets<BM, BN, NW, MW>& o, const StepSrc& src, uint8_t* dst,
+                                         int wave, int part, int nparts, int t)
+{
+    typedef StageGeom<BM, BN, NW> G;
+    int n = 0;
 #pragma unroll
-            for (int i = 0; i < GA; ++i)
+    for (int j = 0; j < G::JA; ++j)
+        if (j % nparts == part && n++ == t && (G::IA % NW == 0 || wave + j * NW < G::IA))
+            dma16(src.a + o.a[j], dst + (wave + j * NW) * 1024);
 #pragma unroll
-                for (int j = 0; j < GB; ++j) {
-                    const int col = out_col(j);
+    for (int j = 0; j < G::JB; ++j)
+        if (j % nparts == part && n++ == t && (G::IB % NW == 0 || wave + j * NW < G::IB))
+            dma16(src.b + o.b[j], dst + G::A_BYTES + (wave + j * NW) * 1024);
 #pragma unroll
-                    for (int v = 0; v < NACC; ++v) {
-                        const int row = out_row(i, v);
-                        if (row < p.rows && col < p.N)
-                            p.c[(int64_t)row * p.N + col] = f32_to_bf16_rne(acc[i][j][v]);
-                    }
+    for (int j = 0; j < G::KSA; ++j)
+        if (j % nparts == part && n++ == t && (G::ISA % NW == 0 || wave + j * NW < G::ISA))
+            dma4(src.as + o.as[j], dst + G::SA_OFF + (wave + j * NW) * 256);
+#pragma unroll
+    for (int j = 0; j < G::KSB; ++j)
+        if ((j + 1) % nparts == part && n++ == t && (G::ISB % NW == 0 || wave + j * NW < G::ISB))
+            dma4(src.bs + o.bs[j], dst + G::SB_OFF + (wave + j * NW) * 256);
+}
+
+template <int BM, int BN, int NW>
+__host__ __device__ constexpr int copies_in_part(int part, int nparts)
+{
+    typedef StageGeom<BM, BN, NW> G;
+    int n = 0;
+    for (int j = 0; j < G::JA; ++j)
+        n += j % nparts == part;
+    for (int j = 0; j < G::JB; ++j)
+        n += j % nparts == part;
+    for (int j = 0; j < G::KSA; ++j)
+        n += j % nparts == part;
+    for (int j = 0; j < G::KSB; ++j)
+        n += (j + 1) % nparts == part;
+    return n;
+}
+
+// Exact block-scaled GEMM on v_mfma_f32_32x32x16_bf16, software-pipelined.
+//
+// One wave per SIMD, WGM x WGN waves of (BM / WGM) x (BN / WGN); large wave
+// tiles keep the conversion work per MFMA low (each code a wave reads feeds
+// BN / WGN resp. BM / WGM outputs).  A K-step (128 K) is four sub-steps of
+// one MX block (32 K).  Lane group h = lane / 32 takes K [32j + 16h + 8m,
+// +8) in MFMA m = 0, 1 of sub-step j, the same assignment for A and B, so
+// one 16-byte read of logical chunk 2j + h feeds both MFMAs.
+//
+// Pipeline, per fragment (32 rows of A or B): while the MFMAs of sub-step j
+// run, the fragment's codes of sub-step j + 1 (already in registers) are
+// converted to bfloat16 with the block scale folded in (exact), and its
+// codes of sub-step j + 2 are read from LDS into the freed registers.  A
+// fragments are converted in place right after the MFMA group that used
+// them; B fragments, used by every group, are double-buffered.  The one
+// barrier of a K-step sits at sub-step 2: after it the copy of step s + 2
+// reuses the stage just finished, and sub-steps 2 and 3 read the first
+// codes of step s + 1.  The MFMAs take the B fragment as their first
+// operand, so a lane's accumulators hold four consecutive columns of C.
+template <int BM, int BN, int WGM, int WGN, int OCC>
+__global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+mxgemm_exact_kernel(GemmArgs p)
+{
+    constexpr int MW = 32;
+    constexpr int NW = WGM * WGN;
+    constexpr int TM = BM / WGM, TN = BN / WGN;
+    constexpr int GA = TM / MW, GB = TN / MW;
+    constexpr int NF = GA + GB;            // fragments a wave reads per sub-step
+    static_assert(TM % MW == 0 && TN % MW == 0, "wave tile must be a multiple of the MFMA width");
+    static_assert(GB <= GA && GA % GB == 0, "B fragments are spread evenly over the A groups");
+    // upper bound of the work slices of one MFMA group (see kstep)
+    constexpr int kMaxTasks = 20 + StageGeom<BM, BN, NW>::JA + StageGeom<BM, BN, NW>::JB + 4 + 2;
+    typedef StageGeom<BM, BN, NW> G;
+
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[G::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int lr = lane & 31, lq = lane >> 5;
+
+    // Byte offsets in a stage of the lane's first A and B fragment rows and
+    // of their scale words; fragment bases are multiples of 32 rows, so the
+    // swizzle key of every row is that of lr.
+    const int a_row = (wm * TM + lr) * kBK;
+    const int b_row = G::A_BYTES + (wn * TN + lr) * kBK;
+    const int sa_row = G::SA_OFF + (wm * TM + lr) * 4;
+    const int sb_row = G::SB_OFF + (wn * TN + lr) * 4;
+    auto frag_off = [&](int f) { return f < GA ? a_row + f * MW * kBK : b_row + (f - GA) * MW * kBK; };
+    auto scale_off = [&](int f) { return f < GA ? sa_row + f * MW * 4 : sb_row + (f - GA) * MW * 4; };
+    auto chunk_off = [&](int j) { return swz_t<MW>(lr, 2 * j + lq) * 16; };
+
+    // one work item per work-group (the dispatcher does the load balancing;
+    // a persistent loop would hold the epilogue's per-lane address terms in
+    // registers across the K loop)
+    const int w = remap_block(blockIdx.x, gridDim.x);
+    if (w >= p.total_work)
+        return;
+    {
+        const TileCoord tc = decode_work(w, p.tiles_m, p.tiles_n, p.split, p.group_n);
+        const int m0 = tc.tm * BM, n0 = tc.tn * BN;
+        CopyOffsets<BM, BN, NW, MW> co;
+        copy_offsets(p, m0, n0, wave, lane, co);
+        const int seg0 = tc.ks * p.segs_per_split;
+        const int nsteps = p.segs_per_split * (p.kpr / kBK);
+
+        v16f acc[GA][GB];
+#pragma unroll
+        for (int i = 0; i < GA; ++i)
+#pragma unroll
+            for (int g = 0; g < GB; ++g)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[i][g][v] = 0.f;
+
+        u32x4 raw[NF];             // codes of the sub-step after the next
+        u32x4 cva[GA][2];          // A operands (bfloat16 pairs) of the current sub-step
+        u32x4 cvb[2][GB][2];       // B operands, by sub-step parity
+        uint32_t sw[NF];           // scale words (4 MX blocks) of a K-step
+
+        copy_issue(co, step_src(p, seg0, n0, 0), stage0, wave);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (nsteps > 1)
+            copy_issue(co, step_src(p, seg0, n0, 1), stage1, wave);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            sw[f] = *reinterpret_cast<const uint32_t*>(stage0 + scale_off(f));
+            raw[f] = *reinterpret_cast<const u32x4*>(stage0 + frag_off(f) + chunk_off(0));
+        }
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+            const float sc = e8m0_to_f32(sw[f]);
+            u32x4(&dst)[2] = f < GA ? cva[f] : cvb[0][f - GA];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                dst[e >> 2][e & 3] = cvt_word(raw[f], sc, e);
+            raw[f] = *reinterpret_cast<const u32x4*>(stage0 + frag_off(f) + chunk_off(1));
+        }
+
+        // Group i of a sub-step: the 2 GB MFMAs of A fragment i, each
+        // followed by a slice of the group's other work, in this order:
+        //   A fragment i: scale, 8 conversions (next sub-step), LDS read
+        //     (the sub-step after);
+        //   the B fragments assigned to group i: the same;
+        //   at sub-step 2: this group's share of the copies of step s + 2,
+        //     and the scale words of step s + 1 for fragments f = i mod GA.
+        // sched_barrier fences keep that order, so the conversions run in
+        // the MFMAs' shadow.
+        auto kstep = [&](int s, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+            // Past the last K-step the copies repeat the last one (into the
+            // stage just released, never read again): no branches here.
+            const StepSrc src2 = step_src(p, seg0, n0, s + 2 < nsteps ? s + 2 : nsteps - 1);
+            uint32_t swn[NF];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = j & 1;
+                if (j == 2) {
+                    // every wave has read all of CUR and has its copies of
+                    // step s + 1 in NXT
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    __syncthreads();
                 }
-        } else {
-            // Split-K: every split stores its FP32 partial tile; the last
-            // split to arrive sums all partials in split order (so the
-            // result does not depend on arrival order) and writes C.
-            constexpr int NQ = NACC / 4;
-            const int tile_id = tc.tm * p.tiles_n + tc.tn;
-            float* wsp = p.ws + ((int64_t)tile_id * p.split + tc.ks) * (BM * BN);
+                // Sub-steps j + 1, j + 2 are converted and read even past
+                // the last K-step (then from the idle stage NXT; the values
+                // are never used), which keeps this code branch-free.
+                const uint8_t* src = j < 2 ? cur : nxt;
+                const int coff = chunk_off((j + 2) & 3);
+                const int jn = (j + 1) & 3;
 #pragma unroll
-            for (int i = 0; i < GA; ++i)
+                for (int i = 0; i < GA; ++i) {
+                    constexpr int NU = 2 * GB;                        // MFMAs in the group
+                    constexpr int RB = GA / GB;                       // groups per B fragment
+                    const int nbf = i % RB == 0 ? 1 : 0;              // B fragment i / RB is the group's
+                    const int gb = i / RB;
+                    const int ncopy = j == 2 ? copies_in_part<BM, BN, NW>(i, GA) : 0;
+                    const int nsw = j == 2 ? 1 + (i + GA < NF ? 1 : 0) : 0;   // fragments i, i + GA
+                    const int ntask = 10 * (1 + nbf) + ncopy + nsw;
+                    u32x4 cva_n[2];
+                    float sc = 0.f;
 #pragma unroll
-                for (int j = 0; j < GB; ++j)
+                    for (int u = 0; u < NU; ++u) {
+                        const int m = u / GB, g = u % GB;
+                        acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(v8bf, cvb[c][g][m]), __builtin_bit_cast(v8bf, cva[i][m]),
+                            acc[i][g], 0, 0, 0);
+                        const int t0 = u * ntask / NU, t1 = (u + 1) * ntask / NU;
 #pragma unroll
-                    for (int q = 0; q < NQ; ++q)
-                        *reinterpret_cast<v4f*>(wsp + (((i * GB + j) * NQ + q) * NT + tid) * 4) =
-                            v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                acc[i][j][4 * q + 3]};
-            __threadfence();
-            __syncthreads();
-            if (tid == 0) {
-                const int old = atomicAdd(p.counters + tile_id, 1);
-                s_last = (old == p.split - 1);
-            }
-            __syncthreads();
-            if (s_last) {
-                __threadfence();
-                const float* wst = p.ws + (int64_t)tile_id * p.split * (BM * BN);
-#pragma unroll
-                for (int i = 0; i < GA; ++i)
-#pragma unroll
-                    for (int j = 0; j < GB; ++j) {
-                        const int col = out_col(j);
-#pragma unroll
-                        for (int q = 0; q < NQ; ++q) {
-                            const int64_t off = (((i * GB + j) * NQ + q) * NT + tid) * 4;
-                            v4f sum = *reinterpret_cast<const v4f*>(wst + off);
-                            for (int s = 1; s < p.split; ++s) {
-                                const v4f t = *reinterpret_cast<const v4f*>(wst + (int64_t)s * (BM * BN) + off);
-                                sum[0] += t[0];
-                                sum[1] += t[1];
-                                sum[2] += t[2];
-                                sum[3] += t[3];
-                            }
-#pragma unroll
-                            for (int u = 0; u < 4; ++u) {
-                                const int row = out_row(i, 4 * q + u);
-                                if (row < p.rows && col < p.N)
-                                    p.c[(int64_t)row * p.N + col] = f32_to_bf16_rne(sum[u]);
+                        for (int t = 0; t < kMaxTasks; ++t) {
+                            if (t < t0 || t >= t1)
+                                continue;
+                            if (t < 10) {                              // A fragment i
+                                if (t == 0)
+                                    sc = e8m0_to_f32(sw[i] >> (8 * jn));
+                                else if (t < 9)
+                                    cva_n[(t - 1) >> 2][(t - 1) & 3] = cvt_word(raw[i], sc, t - 1);
+                                else
+                                    raw[i] = *reinterpret_cast<const u32x4*>(src + frag_off(i) + coff);
+                            } else if (t < 10 * (1 + nbf)) {           // B fragment gb
+                                const int tb = t - 10;
+                                if (tb == 0)
+                                    sc = e8m0_to_f32(sw[GA + gb] >> (8 * jn));
+                                else if (tb < 9)
+                                    cvb[c ^ 1][gb][(tb - 1) >> 2][(tb - 1) & 3] = cvt_word(raw[GA + gb], sc, tb - 1);
+                                else
+                                    raw[GA + gb] = *reinterpret_cast<const u32x4*>(src + frag_off(GA + gb) + coff);
+                            } else if (t < 10 * (1 + nbf) + ncopy) {   // copies of step s + 2
+                                copy_one(co, src2, const_cast<uint8_t*>(cur), wave, i, GA, t - 10 * (1 + nbf));
+                            } else {                                   // scale words of step s + 1
+                                const int f2 = i + GA * (t - 10 * (1 + nbf) - ncopy);
+                                swn[f2] = *reinterpret_cast<const uint32_t*>(nxt + scale_off(f2));
                             }
                         }
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                if (tid == 0)
-                    atomicExch(p.counters + tile_id, 0);
+                    cva[i][0] = cva_n[0];
+                    cva[i][1] = cva_n[1];
+                }
+                if (j == 2) {
+#pragma unroll
+                    for (int f = 0; f < NF; ++f)
+                        sw[f] = swn[f];
+                }
             }
+        };
+        int s = 0;
+        for (; s + 1 < nsteps; s += 2) {
+            kstep(s, stage0, stage1);
+            kstep(s + 1, stage1, stage0);
         }
+        if (s < nsteps)
+            kstep(s, stage0, stage1);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the work-group
+
+        store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
     }
 }
 
 template <int BM, int BN, int WGM, int WGN, int OCC, int MW>
-static hipError_t launch_cfg(const GemmArgs& a, int grid, bool exact, hipStream_t stream)
+static hipError_t launch_cfg(const GemmArgs& a, bool exact, hipStream_t stream)
 {
     if (exact)
-        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, true, MW>), dim3(grid),
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, true, MW>), dim3(a.total_work),
                            dim3(WGM * WGN * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, false, MW>), dim3(grid),
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, false, MW>), dim3(a.total_work),
                            dim3(WGM * WGN * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, int grid, hipStream_t stream)
+// Large tiles: native on the scaled MFMA kernel (NWM x NWN waves), exact on
+// the pipelined bf16 kernel (EWM x EWN waves, one per SIMD).
+template <int BM, int BN, int NWM, int NWN, int NOCC, int EWM, int EWN>
+static hipError_t launch_large(const GemmArgs& a, bool exact, hipStream_t stream)
+{
+    if (exact)
+        hipLaunchKernelGGL((mxgemm_exact_kernel<BM, BN, EWM, EWN, 1>), dim3(a.total_work), dim3(EWM * EWN * 64), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, NWM, NWN, NOCC, false, 32>), dim3(a.total_work),
+                           dim3(NWM * NWN * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, hipStream_t stream)
 {
     switch (cfg) {
-    case 0: return launch_cfg<256, 256, 2, 4, 2, 32>(a, grid, exact, stream);
-    case 1: return launch_cfg<256, 128, 2, 2, 1, 32>(a, grid, exact, stream);
-    case 2: return launch_cfg<128, 128, 2, 2, 1, 32>(a, grid, exact, stream);
-    case 3: return launch_cfg<64, 64, 2, 2, 4, 16>(a, grid, exact, stream);
-    case 4: return launch_cfg<32, 64, 1, 4, 4, 16>(a, grid, exact, stream);
-    case 5: return launch_cfg<16, 64, 1, 4, 4, 16>(a, grid, exact, stream);
+    case 0: return launch_large<256, 256, 2, 4, 2, 2, 2>(a, exact, stream);
+    case 1: return launch_large<256, 128, 2, 2, 1, 2, 2>(a, exact, stream);
+    case 2: return launch_large<128, 128, 2, 2, 1, 2, 2>(a, exact, stream);
+    case 3: return launch_cfg<64, 64, 2, 2, 4, 16>(a, exact, stream);
+    case 4: return launch_cfg<32, 64, 1, 4, 4, 16>(a, exact, stream);
+    case 5: return launch_cfg<16, 64, 1, 4, 4, 16>(a, exact, stream);
     default: return hipErrorInvalidValue;
     }
 }
+
 
 // ------------------------------------------------------------- quantiser --
 

@@ -89,10 +89,15 @@ double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int s
     // with the other resident work-groups, plus fixed start-up cost
     const double flops = 2.0 * t.tile_m * t.tile_n * (double)(K / split);
     const double peak = exact ? 4096.0 : 8192.0;   // FLOP per clock per CU
-    double item = flops / (peak * t.rel_rate) * t.blocks_per_cu + 3000.0;
-    if (split > 1)
-        item += (double)t.tile_m * t.tile_n * 4.0 * 3.0 / 64.0;   // partial write + fix-up
-    return (double)rounds * item;
+    const double item = flops / (peak * t.rel_rate) * t.blocks_per_cu + 3000.0;
+    double total = (double)rounds * item;
+    if (split > 1) {
+        // FP32 partials written and read back, C written, by a second
+        // launch: bytes at ~4 TB/s in 2.4 GHz clocks, plus the launch
+        const double bytes = (double)rows * N * (8.0 * split + 2.0);
+        total += bytes / 4e12 * 2.4e9 + 5000.0;
+    }
+    return total;
 }
 
 int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N, int64_t cms,
@@ -190,12 +195,11 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     if (work >= (1LL << 31))
         return fail(MXGEMM_EUNSUPPORTED, "too many work items");
     p->work_items = (int32_t)work;
-    int64_t grid = (int64_t)num_cus * t.blocks_per_cu;
-    if (opts && opts->grid > 0 && opts->grid < grid)
-        grid = opts->grid;
-    p->grid = (int32_t)(work < grid ? work : grid);
-    // zigzag group width: about a square patch of tiles per XCD per round
-    const int64_t per_xcd = ceil_div(p->grid, mxg::kNumXcd) / p->split;
+    p->grid = (int32_t)work;
+    // zigzag group width: about a square patch of tiles per XCD per round of
+    // resident work-groups
+    const int64_t resident = (int64_t)num_cus * t.blocks_per_cu;
+    const int64_t per_xcd = ceil_div(work < resident ? work : resident, mxg::kNumXcd) / p->split;
     int g = (int)floor(sqrt((double)(per_xcd > 1 ? per_xcd : 1)));
     if (g < 1)
         g = 1;
@@ -204,9 +208,7 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     p->group_n = g;
     p->slot_bytes = (int64_t)R * cms * kpr;
     p->scale_slot_bytes = (int64_t)R * cms * (kpr / 32);
-    p->workspace_bytes = p->split > 1
-        ? (int64_t)p->tiles_m * p->tiles_n * p->split * t.tile_m * t.tile_n * 4 : 0;
-    p->counter_count = (int64_t)p->tiles_m * p->tiles_n;
+    p->workspace_bytes = p->split > 1 ? (int64_t)p->split * rows * N * 4 : 0;
     return MXGEMM_OK;
 }
 
@@ -218,7 +220,6 @@ struct mxgemm_seg {
     uint8_t* ring;
     uint8_t* sring;
     float* ws;
-    int* counters;
     hipStream_t side;
     hipEvent_t start;
     std::vector<hipEvent_t> ready, credit;
@@ -254,8 +255,6 @@ void release(mxgemm_seg* h)
         (void)hipFree(h->sring);
     if (h->ws)
         (void)hipFree(h->ws);
-    if (h->counters)
-        (void)hipFree(h->counters);
     delete h;
 }
 
@@ -308,7 +307,7 @@ int mxgemm_seg_decode(const mxgemm_seg_plan_t* plan, int64_t rows, int32_t w, in
         return fail(MXGEMM_EINVAL, "bad plan or rows");
     const int tiles_m = (int)ceil_div(rows, plan->tile_m);
     const int total = tiles_m * plan->tiles_n * plan->split;
-    const int grid = total < plan->grid ? total : plan->grid;
+    const int grid = total;   // one work-group per work item
     if (w < 0 || w >= total || block < 0 || block >= grid)
         return fail(MXGEMM_EINVAL, "work item or block out of range");
     const mxg::TileCoord c = mxg::decode_work(w, tiles_m, plan->tiles_n, plan->split, plan->group_n);
@@ -360,12 +359,7 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
         return oom("staging scale ring", sring_bytes);
     if (plan.workspace_bytes > 0 && hipMalloc((void**)&h->ws, plan.workspace_bytes) != hipSuccess)
         return oom("split-K workspace", plan.workspace_bytes);
-    const size_t cnt_bytes = (size_t)plan.counter_count * sizeof(int);
-    if (hipMalloc((void**)&h->counters, cnt_bytes) != hipSuccess)
-        return oom("split-K counters", cnt_bytes);
-    hipError_t e = hipMemset(h->counters, 0, cnt_bytes);
-    if (e == hipSuccess)
-        e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    hipError_t e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
     if (e == hipSuccess)
         e = hipEventCreateWithFlags(&h->start, hipEventDisableTiming);
     h->ready.assign(plan.window_slots, nullptr);
@@ -425,8 +419,6 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
     HIP_TRY(hipEventRecord(h->start, st));
     HIP_TRY(hipStreamWaitEvent(h->side, h->start, 0));
 
-    const mxg::TileCfg& t = mxg::tile_cfg(P.tile_cfg);
-    const int64_t cap = (int64_t)P.num_cus * t.blocks_per_cu;
     for (int w = 0; w < P.windows; ++w) {
         const int chunk0 = w * P.chunks_per_window;
         const int left = P.chunks - chunk0;
@@ -469,7 +461,6 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         ga.bs = (const uint8_t*)b_scale;
         ga.c = (uint16_t*)c + (int64_t)chunk0 * P.commMSize * P.N;
         ga.ws = h->ws;
-        ga.counters = h->counters;
         ga.rows = (int)rows;
         ga.N = (int)P.N;
         ga.K = (int)P.K;
@@ -481,12 +472,20 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         ga.segs_per_split = P.rank_size / P.split;
         ga.group_n = P.group_n;
         ga.total_work = ga.tiles_m * ga.tiles_n * ga.split;
-        int64_t grid = ga.total_work < P.grid ? ga.total_work : P.grid;
-        if (grid > cap)
-            grid = cap;
+        ga.c_vec4 = ((uintptr_t)ga.c % 8 == 0) && (P.N % 4 == 0);
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[2 * w], st));
-        HIP_TRY(mxg::launch_gemm(P.tile_cfg, P.precision == MXGEMM_PRECISION_EXACT, ga, (int)grid, st));
+        HIP_TRY(mxg::launch_gemm(P.tile_cfg, P.precision == MXGEMM_PRECISION_EXACT, ga, st));
+        if (P.split > 1) {
+            mxg::ReduceArgs ra;
+            ra.ws = h->ws;
+            ra.c = ga.c;
+            ra.rows = ga.rows;
+            ra.N = ga.N;
+            ra.split = P.split;
+            ra.c_vec4 = ga.c_vec4;
+            HIP_TRY(mxg::launch_reduce(ra, st));
+        }
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
         HIP_TRY(hipEventRecord(h->credit[g], st));

@@ -65,18 +65,18 @@ def test_plan_options_rules():
 def _check_bijection(p, rows):
     tiles_m = -(-rows // p.tile_m)
     total = tiles_m * p.tiles_n * p.split
-    grid = min(total, p.grid)
     seen = set()
     for w in range(total):
         tm, tn, ks, _ = pkg.decode(p, rows, w, 0)
         assert 0 <= tm < tiles_m and 0 <= tn < p.tiles_n and 0 <= ks < p.split
         seen.add((tm, tn, ks))
     assert len(seen) == total
-    # every work item is reached by exactly one block of the persistent grid
-    starts = [pkg.decode(p, rows, 0, b)[3] for b in range(grid)]
-    assert sorted(starts) == list(range(grid))
-    covered = sorted(w for s in starts for w in range(s, total, grid))
-    assert covered == list(range(total))
+    # the launch has one work-group per work item and the XCD remap is a
+    # permutation: every work item is taken by exactly one work-group
+    taken = [pkg.decode(p, rows, 0, b)[3] for b in range(total)]
+    assert sorted(taken) == list(range(total))
+    with pytest.raises(pkg.MxgemmError):
+        pkg.decode(p, rows, 0, total)
 
 
 @pytest.mark.parametrize("name", list(inputs.WORKLOADS))
@@ -100,14 +100,14 @@ def test_schedule_bijection_forced(cfg, split):
 
 
 def test_xcd_remap_groups_blocks_per_xcd():
-    # with a grid that is a multiple of 8, the blocks of XCD x (b % 8 == x)
-    # start from one contiguous run of logical work IDs
+    # the work-groups of XCD x (b % 8 == x) take one contiguous run of
+    # logical work IDs, in dispatch order
     p = pkg.plan(8192, 1024, 8, 8192, 512, 4)
-    assert p.grid % 8 == 0
     rows = p.chunks_per_window * 512
+    assert p.grid == p.work_items
     for x in range(8):
-        starts = sorted(pkg.decode(p, rows, 0, b)[3] for b in range(x, p.grid, 8))
-        assert starts == list(range(starts[0], starts[0] + len(starts)))
+        taken = [pkg.decode(p, rows, 0, b)[3] for b in range(x, p.grid, 8)]
+        assert taken == list(range(taken[0], taken[0] + len(taken)))
 
 
 def test_zigzag_reverses_m_on_odd_groups():
