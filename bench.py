@@ -97,7 +97,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time steps issued on the stream (default: replays of one captured step)")
     ap.add_argument("--tile-cfg", type=int, default=-1)
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--window", type=int, default=-1)
@@ -170,25 +171,13 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ---- timed: stream timer --------------------------------------------
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        flush_caches()
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_mean = statistics.mean(ms)
-    log(f"[bench] stream: mean {ms_mean:.4f} ms median {statistics.median(ms):.4f} "
-        f"min {min(ms):.4f} max {max(ms):.4f}")
-
-    # ---- graph timer -----------------------------------------------------
-    graph_ms = None
+    # ---- timed steps ------------------------------------------------------
+    # Each step is one run() of the whole path.  By default the step is
+    # captured once into a HIP graph and the K timed steps are replays of it
+    # (how a serving loop issues a fixed-shape call); --no-graph times steps
+    # issued on the stream.  Either way a 512 MiB fill precedes every step
+    # (outside its events) so no step starts with warm caches.
+    graph = None
     if not args.no_graph:
         try:
             gs = torch.cuda.Stream()
@@ -198,21 +187,41 @@ def main():
                 with torch.cuda.graph(graph, stream=gs):
                     g.run(a_q, a_s, b_q, b_s, c, stream=gs)
             torch.cuda.synchronize()
-            gms = []
-            for i in range(args.steps):
+            for _ in range(max(1, args.warmup)):
                 flush_caches()
-                s0 = torch.cuda.Event(enable_timing=True)
-                s1 = torch.cuda.Event(enable_timing=True)
-                s0.record(stream)
                 graph.replay()
-                s1.record(stream)
-                torch.cuda.synchronize()
-                gms.append(s0.elapsed_time(s1))
-            graph_ms = statistics.median(gms)
-            log(f"[bench] graph: median {graph_ms:.4f} ms")
-            del graph
-        except Exception as e:  # report, keep the stream number
-            log(f"[bench] graph timer unavailable: {e}")
+            torch.cuda.synchronize()
+        except Exception as e:  # report, fall back to stream issue
+            log(f"[bench] graph capture unavailable ({e}); timing stream-issued steps")
+            graph = None
+
+    def timed(replay):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            flush_caches()
+            starts[i].record(stream)
+            if replay:
+                graph.replay()
+            else:
+                step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) for s, e in zip(starts, ends)], time.perf_counter() - t0
+
+    ms, wall = timed(graph is not None)
+    ms_mean = statistics.mean(ms)
+    timer = "graph" if graph is not None else "stream"
+    log(f"[bench] {timer}: mean {ms_mean:.4f} ms median {statistics.median(ms):.4f} "
+        f"min {min(ms):.4f} max {max(ms):.4f}")
+    stream_ms = None
+    if graph is not None:
+        sms, _ = timed(False)
+        stream_ms = statistics.mean(sms)
+        log(f"[bench] stream-issued: mean {stream_ms:.4f} ms")
+        del graph
 
     # ---- per-kernel durations (HIP events around each launch) -----------
     g.set_profiling(True)
@@ -227,8 +236,20 @@ def main():
     stage_ms_per_launch = kt["stage_ms"] / kt["stage_launches"]
     flops = float(w.flops)
     flops_per_launch = flops / plan["windows"]
-    achieved = flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
+    # algorithmic bytes of one GEMM launch (a window of M / windows rows on
+    # average): A rows and B with their E8M0 scales, C in bfloat16
+    rows_w = w.M / plan["windows"]
+    bytes_per_launch = (rows_w * w.K + w.N * w.K) * 33 / 32 + rows_w * w.N * 2
     kernel_peak = PEAK_BF16_TFLOPS if args.precision == "exact" else PEAK_FP8_TFLOPS
+    # the roofline that bounds the launch: HBM when its arithmetic intensity
+    # is below the ridge point of the MFMA form it uses
+    hbm_bound = flops_per_launch / bytes_per_launch < kernel_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if hbm_bound:
+        achieved = bytes_per_launch / (gemm_ms_per_launch * 1e-3) / 1e9
+        roof_peak, roof_unit = PEAK_HBM_GBS, "GB/s"
+    else:
+        achieved = flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
+        roof_peak, roof_unit = kernel_peak, "TFLOP/s"
     log(f"[bench] kernels: gemm {gemm_ms_per_launch * 1e3:.2f} us/launch x{plan['windows']}, "
         f"stage {stage_ms_per_launch * 1e3:.2f} us/launch")
 
@@ -259,20 +280,24 @@ def main():
                                                  "windows", "grid")}},
         "pct_of_mxfp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "hbm_frac_end_to_end": round(w.algorithmic_bytes / (ms_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "timer": "stream (HIP events per step, 512 MiB cache flush before each step)"
-                 if not args.no_flush else "stream (HIP events per step, warm caches)",
-        "graph_ms_per_step_median": round(graph_ms, 5) if graph_ms is not None else None,
+        "timer": (("replays of one HIP-graph-captured step" if timer == "graph" else "stream-issued steps")
+                  + ", HIP events per step" + (", 512 MiB cache flush before each step"
+                                                 if not args.no_flush else ", warm caches")),
+        "stream_issued_ms_per_step": round(stream_ms, 5) if stream_ms is not None else None,
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "precision": args.precision,
         "roofline": {
-            "bound": "mfma",
-            "kernel": "mxgemm_kernel (" + ("bf16 MFMA, exact products" if args.precision == "exact"
-                                           else "scaled FP8 MFMA") + ")",
+            "bound": "hbm" if hbm_bound else "mfma",
+            "kernel": "GEMM kernel (" + ("bf16 MFMA, exact products" if args.precision == "exact"
+                                         else "scaled FP8 MFMA") + ")",
             "achieved": round(achieved, 3),
-            "peak": kernel_peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / kernel_peak, 4),
-            "frac_of_mxfp8_peak": round(achieved / PEAK_FP8_TFLOPS, 4),
+            "peak": roof_peak,
+            "unit": roof_unit,
+            "frac": round(achieved / roof_peak, 4),
+            "gemm_tflops": round(flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12, 3),
+            "frac_of_mxfp8_peak": round(flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
+                                        / PEAK_FP8_TFLOPS, 4),
+            "bytes_per_launch": int(bytes_per_launch),
             "traffic": traffic,
             "gemm_us_per_launch": round(gemm_ms_per_launch * 1e3, 3),
             "launches_per_step": plan["windows"],

@@ -195,7 +195,8 @@ int mxgemm_quantize_mxfp8(const float* x, int64_t rows, int64_t cols, int64_t ld
 
 /*
  * Kernel timing for measurement.  While enabled, run() brackets every GEMM
- * launch (on `stream`) and every staging launch (on the side stream) with
+ * kernel launch (on `stream`; with S > 1 the split-K reduction after it is
+ * outside the bracket) and every staging launch (on the side stream) with
  * timing events.  mxgemm_seg_kernel_times synchronises the handle and
  * returns the summed durations (ms) and launch counts since the last call,
  * then resets them.  Not for use under graph capture.  Errors: EINVAL, EHIP.

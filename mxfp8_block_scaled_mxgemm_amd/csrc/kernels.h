@@ -13,10 +13,15 @@ struct TileCfg {
     int lds_bytes;          // LDS per work-group
     int blocks_per_cu;      // resident work-groups per compute unit
     float rel_rate;         // planner's relative MFMA efficiency estimate
+    int steps_per_stage;    // K-steps of 128 copied per LDS stage
 };
 
 int num_tile_cfgs();
 const TileCfg& tile_cfg(int i);
+// Tile configuration whose work items copy their whole K range at once;
+// usable only when a work item has at most kOneShotSteps K-steps of 128.
+constexpr int kOneShotCfg = 6;
+constexpr int kOneShotSteps = 8;
 
 // Staging copy for one window: chunks [chunk0, chunk0 + nch) of every
 // segment, data and scales, into ring slots chunk % nbuf.

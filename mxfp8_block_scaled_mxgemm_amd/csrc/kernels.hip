@@ -20,20 +20,24 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // accumulator element v.
 constexpr int kBK = 128;
 
-template <int BM, int BN>
+// LDS of a work-group: two stages of CH K-steps
+template <int BM, int BN, int CH>
 constexpr int lds_bytes_for()
 {
-    return 2 * (BM * kBK + BN * kBK + 4 * (BM > 64 ? BM : 64) + 4 * (BN > 64 ? BN : 64));
+    return 2 * CH * (BM * kBK + BN * kBK + 4 * (BM > 64 ? BM : 64) + 4 * (BN > 64 ? BN : 64));
 }
 
 static const TileCfg kCfgs[] = {
-    // rel_rate: measured throughput per CU relative to the 256x256 tile
-    {256, 256, 512, lds_bytes_for<256, 256>(), 1, 1.00f},
-    {256, 128, 256, lds_bytes_for<256, 128>(), 1, 0.69f},
-    {128, 128, 256, lds_bytes_for<128, 128>(), 1, 0.53f},
-    {64, 64, 256, lds_bytes_for<64, 64>(), 4, 0.30f},
-    {32, 64, 256, lds_bytes_for<32, 64>(), 4, 0.20f},
-    {16, 64, 256, lds_bytes_for<16, 64>(), 4, 0.12f},
+    // rel_rate: planner's throughput per CU relative to the 256x256 tile
+    // (threads: exact form; the native 256x256 form runs 512)
+    {256, 256, 256, lds_bytes_for<256, 256, 1>(), 1, 1.00f, 1},
+    {256, 128, 256, lds_bytes_for<256, 128, 1>(), 1, 0.89f, 1},
+    {128, 128, 256, lds_bytes_for<128, 128, 1>(), 1, 0.53f, 1},
+    {64, 64, 256, lds_bytes_for<64, 64, 2>(), 2, 0.30f, 2},
+    {32, 64, 256, lds_bytes_for<32, 64, 3>(), 2, 0.20f, 3},
+    {16, 64, 256, lds_bytes_for<16, 64, 3>(), 2, 0.12f, 3},
+    // one stage holding a work item's whole K range (at most kOneShotSteps)
+    {32, 64, 256, lds_bytes_for<32, 64, kOneShotSteps>() / 2, 1, 0.20f, kOneShotSteps},
 };
 
 int num_tile_cfgs() { return (int)(sizeof(kCfgs) / sizeof(kCfgs[0])); }
@@ -393,8 +397,12 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream)
 }
 
 // Block-scaled GEMM, scaled-MFMA (native) forms and the 16-wide exact form.
-// WGM x WGN waves of (BM / WGM) x (BN / WGN).
-template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT, int MW>
+// WGM x WGN waves of (BM / WGM) x (BN / WGN).  A stage holds CH K-steps, so
+// small tiles keep several K-steps' copies in flight (their K loop is bound
+// by copy latency, not by the MFMAs).  ONE: a work item has at most CH
+// K-steps, all copied at once into a single stage (skinny shapes, where the
+// whole K range of a split fits in LDS).
+template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT, int MW, int CH, bool ONE = false>
 __global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 mxgemm_kernel(GemmArgs p)
 {
@@ -412,8 +420,8 @@ mxgemm_kernel(GemmArgs p)
     // the compiler then knows a step's copies into one stage never alias
     // the reads of the other, and does not wait for the copies before the
     // reads.
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[G::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[CH * G::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[ONE ? 16 : CH * G::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -445,24 +453,34 @@ mxgemm_kernel(GemmArgs p)
                 for (int v = 0; v < NACC; ++v)
                     acc[i][j][v] = 0.f;
 
-        copy_issue(co, step_src(p, seg0, n0, 0), stage0, wave);
+        const int nsup = (nsteps + CH - 1) / CH;    // stages of CH K-steps
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+            if (c < nsteps)
+                copy_issue(co, step_src(p, seg0, n0, c), stage0 + c * G::STAGE, wave);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
 
-        // One K-step: start the copy of step s + 1 into NXT, multiply the
-        // tiles in CUR, then wait for the copy and synchronise.
-        auto kstep = [&](int s, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
-            if (s + 1 < nsteps)
-                copy_issue(co, step_src(p, seg0, n0, s + 1), nxt, wave);
-
+        // One stage: start the copies of stage t + 1 into NXT, multiply the
+        // K-steps in CUR, then wait for the copies and synchronise.
+        auto kstage = [&](int t, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c)
+                if (!ONE && (t + 1) * CH + c < nsteps)
+                    copy_issue(co, step_src(p, seg0, n0, (t + 1) * CH + c), nxt + c * G::STAGE, wave);
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+            if (t * CH + c >= nsteps)
+                break;
+            const uint8_t* sub = cur + c * G::STAGE;
             // Row r of a fragment group is r = group base + lr with the
             // group base a multiple of MW >= 16, so the swizzle key of r
             // equals that of lr: a lane's swizzled byte offsets differ
             // between groups by a constant.
-            const uint8_t* pa = cur + (wm * TM + lr) * kBK;
-            const uint8_t* pb = cur + G::A_BYTES + (wn * TN + lr) * kBK;
-            const uint8_t* psa = cur + G::SA_OFF + (wm * TM + lr) * 4;
-            const uint8_t* psb = cur + G::SB_OFF + (wn * TN + lr) * 4;
+            const uint8_t* pa = sub + (wm * TM + lr) * kBK;
+            const uint8_t* pb = sub + G::A_BYTES + (wn * TN + lr) * kBK;
+            const uint8_t* psa = sub + G::SA_OFF + (wm * TM + lr) * 4;
+            const uint8_t* psb = sub + G::SB_OFF + (wn * TN + lr) * 4;
             auto chunk = [&](int c) { return swz_t<MW>(lr, c) * 16; };
 
             if constexpr (!EXACT && MW == 16) {
@@ -603,13 +621,14 @@ mxgemm_kernel(GemmArgs p)
                 }
             }
 
+            }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
         };
-        for (int s = 0; s < nsteps; s += 2) {
-            kstep(s, stage0, stage1);
-            if (s + 1 < nsteps)
-                kstep(s + 1, stage1, stage0);
+        for (int t = 0; t < nsup; t += 2) {
+            kstage(t, stage0, stage1);
+            if (t + 1 < nsup)
+                kstage(t + 1, stage1, stage0);
         }
 
         store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
@@ -876,14 +895,14 @@ mxgemm_exact_kernel(GemmArgs p)
     }
 }
 
-template <int BM, int BN, int WGM, int WGN, int OCC, int MW>
+template <int BM, int BN, int WGM, int WGN, int OCC, int MW, int CH, bool ONE = false>
 static hipError_t launch_cfg(const GemmArgs& a, bool exact, hipStream_t stream)
 {
     if (exact)
-        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, true, MW>), dim3(a.total_work),
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, true, MW, CH, ONE>), dim3(a.total_work),
                            dim3(WGM * WGN * 64), 0, stream, a);
     else
-        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, false, MW>), dim3(a.total_work),
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, WGM, WGN, OCC, false, MW, CH, ONE>), dim3(a.total_work),
                            dim3(WGM * WGN * 64), 0, stream, a);
     return hipGetLastError();
 }
@@ -897,7 +916,7 @@ static hipError_t launch_large(const GemmArgs& a, bool exact, hipStream_t stream
         hipLaunchKernelGGL((mxgemm_exact_kernel<BM, BN, EWM, EWN, 1>), dim3(a.total_work), dim3(EWM * EWN * 64), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, NWM, NWN, NOCC, false, 32>), dim3(a.total_work),
+        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, NWM, NWN, NOCC, false, 32, 1>), dim3(a.total_work),
                            dim3(NWM * NWN * 64), 0, stream, a);
     return hipGetLastError();
 }
@@ -908,9 +927,10 @@ hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, hipStream_t strea
     case 0: return launch_large<256, 256, 2, 4, 2, 2, 2>(a, exact, stream);
     case 1: return launch_large<256, 128, 2, 2, 1, 2, 2>(a, exact, stream);
     case 2: return launch_large<128, 128, 2, 2, 1, 2, 2>(a, exact, stream);
-    case 3: return launch_cfg<64, 64, 2, 2, 4, 16>(a, exact, stream);
-    case 4: return launch_cfg<32, 64, 1, 4, 4, 16>(a, exact, stream);
-    case 5: return launch_cfg<16, 64, 1, 4, 4, 16>(a, exact, stream);
+    case 3: return launch_cfg<64, 64, 2, 2, 2, 16, 2>(a, exact, stream);
+    case 4: return launch_cfg<32, 64, 1, 4, 2, 16, 3>(a, exact, stream);
+    case 5: return launch_cfg<16, 64, 1, 4, 2, 16, 3>(a, exact, stream);
+    case 6: return launch_cfg<32, 64, 1, 4, 1, 16, kOneShotSteps, true>(a, exact, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -77,7 +77,11 @@ struct Choice {
     double cost;
 };
 
-// Estimated time (arbitrary units) of one window under (cfg, split).
+// Estimated time of one window under (cfg, split), in 2.4 GHz clocks.  A
+// work item is bound either by its MFMAs (at the tile's efficiency, shared
+// with the other resident work-groups of the CU) or by the round trips of
+// its copy stages: a stage's copies are waited for before its K-steps
+// start, and a round trip under load takes ~2 us.
 double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int split,
                 int num_cus, bool exact)
 {
@@ -85,17 +89,20 @@ double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int s
     const int64_t work = tiles * split;
     const int64_t cap = (int64_t)num_cus * t.blocks_per_cu;
     const int64_t rounds = ceil_div(work, cap);
-    // one work item: MFMA cycles at the tile's efficiency, sharing the CU
-    // with the other resident work-groups, plus fixed start-up cost
     const double flops = 2.0 * t.tile_m * t.tile_n * (double)(K / split);
     const double peak = exact ? 4096.0 : 8192.0;   // FLOP per clock per CU
-    const double item = flops / (peak * t.rel_rate) * t.blocks_per_cu + 3000.0;
+    // under a full MFMA load the shader clock settles near 1.5 GHz, so
+    // compute takes ~1.6x its 2.4 GHz cycle count in wall time
+    const double compute = flops / (peak * t.rel_rate) * t.blocks_per_cu * 1.6;
+    const int64_t stages = ceil_div(K / split / 128, t.steps_per_stage);
+    const double copy = (double)stages * 4400.0;
+    const double item = (compute > copy ? compute : copy) + 3000.0;
     double total = (double)rounds * item;
     if (split > 1) {
         // FP32 partials written and read back, C written, by a second
-        // launch: bytes at ~4 TB/s in 2.4 GHz clocks, plus the launch
+        // launch: bytes at ~2.5 TB/s (measured), plus the launch
         const double bytes = (double)rows * N * (8.0 * split + 2.0);
-        total += bytes / 4e12 * 2.4e9 + 5000.0;
+        total += bytes / 2.5e12 * 2.4e9 + 5000.0;
     }
     return total;
 }
@@ -163,6 +170,8 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
                     continue;
                 if (opts && opts->split > 0 && opts->split != s)
                     continue;
+                if (c == mxg::kOneShotCfg && (int64_t)(R / s) * (kpr / 128) > mxg::kOneShotSteps)
+                    continue;   // a work item's K range must fit the single stage
                 const double gemm = estimate(mxg::tile_cfg(c), rows, N, p->K, s, num_cus, exact);
                 const double cost = overlap
                     ? (double)windows * (gemm > stage ? gemm : stage) + stage
@@ -177,7 +186,9 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
         }
     }
     if (best.cfg < 0)
-        return fail(MXGEMM_EINVAL, "no plan satisfies the options (split must divide rank_size)");
+        return fail(MXGEMM_EINVAL, "no plan satisfies the options (split must divide rank_size; "
+                                   "tile_cfg %d needs at most %d K-steps of 128 per split)",
+                    mxg::kOneShotCfg, mxg::kOneShotSteps);
     const int W = best_w;
     p->chunks_per_window = W;
     p->windows = (int32_t)ceil_div(p->chunks, W);
@@ -476,6 +487,8 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[2 * w], st));
         HIP_TRY(mxg::launch_gemm(P.tile_cfg, P.precision == MXGEMM_PRECISION_EXACT, ga, st));
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
         if (P.split > 1) {
             mxg::ReduceArgs ra;
             ra.ws = h->ws;
@@ -486,8 +499,6 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
             ra.c_vec4 = ga.c_vec4;
             HIP_TRY(mxg::launch_reduce(ra, st));
         }
-        if (h->profiling)
-            HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
         HIP_TRY(hipEventRecord(h->credit[g], st));
     }
     if (h->profiling)
