@@ -275,25 +275,66 @@ __device__ __forceinline__ StepSrc step_src(const GemmArgs& p, int seg0, int n0,
 // j % nparts == part), so the issue can be spread between other work.
 template <int BM, int BN, int NW, int MW>
 __device__ __forceinline__ void copy_issue(const CopyOffsets<BM, BN, NW, MW>& o, const StepSrc& src, uint8_t* dst,
-                                           int wave, int part = 0, int nparts = 1)
+                                           int wave, int part = 0, int nparts = 1, uint8_t* pad = nullptr)
 {
     typedef StageGeom<BM, BN, NW> G;
+    // With `pad`, a wave with no piece left in a slot copies 4 bytes per
+    // lane into the 256 bytes at `pad` instead, so every wave issues the
+    // same number of copy instructions (and can count them with vmcnt).
 #pragma unroll
     for (int j = 0; j < G::JA; ++j)
-        if (j % nparts == part && (G::IA % NW == 0 || wave + j * NW < G::IA))
-            dma16(src.a + o.a[j], dst + (wave + j * NW) * 1024);
+        if (j % nparts == part) {
+            if (G::IA % NW == 0 || wave + j * NW < G::IA)
+                dma16(src.a + o.a[j], dst + (wave + j * NW) * 1024);
+            else if (pad)
+                dma4(src.as + o.as[0], pad);
+        }
 #pragma unroll
     for (int j = 0; j < G::JB; ++j)
-        if (j % nparts == part && (G::IB % NW == 0 || wave + j * NW < G::IB))
-            dma16(src.b + o.b[j], dst + G::A_BYTES + (wave + j * NW) * 1024);
+        if (j % nparts == part) {
+            if (G::IB % NW == 0 || wave + j * NW < G::IB)
+                dma16(src.b + o.b[j], dst + G::A_BYTES + (wave + j * NW) * 1024);
+            else if (pad)
+                dma4(src.as + o.as[0], pad);
+        }
 #pragma unroll
     for (int j = 0; j < G::KSA; ++j)
-        if (j % nparts == part && (G::ISA % NW == 0 || wave + j * NW < G::ISA))
-            dma4(src.as + o.as[j], dst + G::SA_OFF + (wave + j * NW) * 256);
+        if (j % nparts == part) {
+            if (G::ISA % NW == 0 || wave + j * NW < G::ISA)
+                dma4(src.as + o.as[j], dst + G::SA_OFF + (wave + j * NW) * 256);
+            else if (pad)
+                dma4(src.as + o.as[0], pad);
+        }
 #pragma unroll
     for (int j = 0; j < G::KSB; ++j)
-        if ((j + 1) % nparts == part && (G::ISB % NW == 0 || wave + j * NW < G::ISB))
-            dma4(src.bs + o.bs[j], dst + G::SB_OFF + (wave + j * NW) * 256);
+        if ((j + 1) % nparts == part) {
+            if (G::ISB % NW == 0 || wave + j * NW < G::ISB)
+                dma4(src.bs + o.bs[j], dst + G::SB_OFF + (wave + j * NW) * 256);
+            else if (pad)
+                dma4(src.as + o.as[0], pad);
+        }
+}
+
+// Wait until at most n of this wave's copy instructions are outstanding
+// (n a compile-time count; vmcnt holds 0..63 on gfx950).
+template <int N>
+__device__ __forceinline__ void wait_copies()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait_copies<r * CPW>() for the runtime r = rem in [0, R]
+template <int CPW, int R>
+__device__ __forceinline__ void wait_steps(int rem)
+{
+    if constexpr (R >= 0) {
+        if (rem == R) {
+            wait_copies<R * CPW>();
+            return;
+        }
+        wait_steps<CPW, R - 1>(rem);
+    }
 }
 
 // Write a wave's accumulators: GA x GB blocks of MW x MW, block (i, j)
@@ -422,6 +463,10 @@ mxgemm_kernel(GemmArgs p)
     // reads.
     __shared__ __attribute__((aligned(1024))) uint8_t stage0[CH * G::STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t stage1[ONE ? 16 : CH * G::STAGE];
+    __shared__ __attribute__((aligned(256))) uint8_t pad_lds[ONE ? 256 : 4];
+    // copy instructions per wave and K-step when padded (ONE)
+    constexpr int kCopiesPerStep = G::JA + G::JB + G::KSA + G::KSB;
+    static_assert(!ONE || (CH - 1) * kCopiesPerStep <= 63, "outstanding copies must fit vmcnt");
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -457,9 +502,12 @@ mxgemm_kernel(GemmArgs p)
 #pragma unroll
         for (int c = 0; c < CH; ++c)
             if (c < nsteps)
-                copy_issue(co, step_src(p, seg0, n0, c), stage0 + c * G::STAGE, wave);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
+                copy_issue(co, step_src(p, seg0, n0, c), stage0 + c * G::STAGE, wave, 0, 1,
+                           ONE ? pad_lds : nullptr);
+        if (!ONE) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+        }
 
         // One stage: start the copies of stage t + 1 into NXT, multiply the
         // K-steps in CUR, then wait for the copies and synchronise.
@@ -472,6 +520,13 @@ mxgemm_kernel(GemmArgs p)
             for (int c = 0; c < CH; ++c) {
             if (t * CH + c >= nsteps)
                 break;
+            if constexpr (ONE) {
+                // all copies were issued up front, in step order: K-step c
+                // has landed once at most (nsteps - 1 - c) steps' copies
+                // are outstanding
+                wait_steps<kCopiesPerStep, CH - 1>(nsteps - 1 - c);
+                __syncthreads();
+            }
             const uint8_t* sub = cur + c * G::STAGE;
             // Row r of a fragment group is r = group base + lr with the
             // group base a multiple of MW >= 16, so the swizzle key of r

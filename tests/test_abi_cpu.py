@@ -131,3 +131,15 @@ def test_plan_ring_geometry():
     assert p.scale_slot_bytes == p.slot_bytes // 32
     assert p.chunks == w.M // w.commMSize
     assert p.window_slots * p.chunks_per_window == w.nbuf
+
+
+def test_one_shot_tile_needs_short_k_range():
+    # configuration 6 copies a work item's whole K range into one stage:
+    # at most 8 K-steps of 128, i.e. (R / split) * kPerRank / 128 <= 8
+    ok = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(tile_cfg=6, split=8))
+    assert ok.tile_cfg == 6 and ok.split == 8
+    with pytest.raises(pkg.MxgemmError):
+        pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(tile_cfg=6, split=4))
+    # the planner never picks it where it does not fit
+    p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(split=1))
+    assert p.tile_cfg != 6
