@@ -60,11 +60,11 @@ class Workload:
 
 
 WORKLOADS: Dict[str, Workload] = {
-    "c1": Workload("c1", 2, 128, 256, 256, 64, 2, 1.0, 0.0, 1.0, 101),
-    "c2": Workload("c2", 4, 1024, 1024, 2048, 256, 2, 1.0, 0.0, 1.0, 102),
-    "c3": Workload("c3", 8, 4096, 896, 4096, 512, 4, 0.5, 0.0, 1.0, 103),
-    "c4": Workload("c4", 8, 64, 896, 2048, 8, 4, 1.0, 0.0, 1.0, 104),
-    "c5": Workload("c5", 8, 8192, 1024, 8192, 512, 4, 1.0, 0.01, 100.0, 105),
+    "tiny_m128_n256_k512": Workload("tiny_m128_n256_k512", 2, 128, 256, 256, 64, 2, 1.0, 0.0, 1.0, 101),
+    "m1024_n2048_k4096": Workload("m1024_n2048_k4096", 4, 1024, 1024, 2048, 256, 2, 1.0, 0.0, 1.0, 102),
+    "m4096_n4096_k7168": Workload("m4096_n4096_k7168", 8, 4096, 896, 4096, 512, 4, 0.5, 0.0, 1.0, 103),
+    "skinny_m64_n2048_k7168": Workload("skinny_m64_n2048_k7168", 8, 64, 896, 2048, 8, 4, 1.0, 0.0, 1.0, 104),
+    "outlier_m8192_n8192_k8192": Workload("outlier_m8192_n8192_k8192", 8, 8192, 1024, 8192, 512, 4, 1.0, 0.01, 100.0, 105),
 }
 
 

@@ -125,7 +125,7 @@ def test_zigzag_reverses_m_on_odd_groups():
 
 
 def test_plan_ring_geometry():
-    w = inputs.WORKLOADS["c5"]
+    w = inputs.WORKLOADS["outlier_m8192_n8192_k8192"]
     p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
     assert p.slot_bytes == w.R * w.commMSize * w.kPerRank
     assert p.scale_slot_bytes == p.slot_bytes // 32

@@ -26,7 +26,7 @@ def _case(name):
 
 # ------------------------------------------------------------- quantiser --
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+@pytest.mark.parametrize("name", ["tiny_m128_n256_k512", "m1024_n2048_k4096", "m4096_n4096_k7168", "skinny_m64_n2048_k7168", "outlier_m8192_n8192_k8192"])
 def test_gpu_quantizer_bit_exact(name):
     torch_cuda()
     case = _case(name)
@@ -94,9 +94,9 @@ def _oracle_full(case, name):
     return _FULL[name]
 
 
-@pytest.mark.parametrize("name,precision", [("c1", "exact"), ("c1", "native"),
-                                            ("c2", "exact"), ("c2", "native"),
-                                            ("c4", "exact"), ("c4", "native")])
+@pytest.mark.parametrize("name,precision", [("tiny_m128_n256_k512", "exact"), ("tiny_m128_n256_k512", "native"),
+                                            ("m1024_n2048_k4096", "exact"), ("m1024_n2048_k4096", "native"),
+                                            ("skinny_m64_n2048_k7168", "exact"), ("skinny_m64_n2048_k7168", "native")])
 def test_parity_full(name, precision):
     torch_cuda()
     case = _case(name)
@@ -108,7 +108,7 @@ def test_parity_full(name, precision):
     assert not bad.any()
 
 
-@pytest.mark.parametrize("name,precision", [("c3", "exact"), ("c3", "native"), ("c5", "exact")])
+@pytest.mark.parametrize("name,precision", [("m4096_n4096_k7168", "exact"), ("m4096_n4096_k7168", "native"), ("outlier_m8192_n8192_k8192", "exact")])
 def test_parity_sampled(name, precision):
     torch_cuda()
     case = _case(name)
@@ -138,7 +138,7 @@ def test_native_mode_on_outlier_data_misses_only_near_zero():
     for such data."""
     torch_cuda()
     import mxfp8_block_scaled_mxgemm_amd as pkg
-    case = _case("c5")
+    case = _case("outlier_m8192_n8192_k8192")
     w = case.w
     got_all = case.run_gpu(opts=_opts("native")).float().cpu().numpy()
     p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
@@ -147,7 +147,7 @@ def test_native_mode_on_outlier_data_misses_only_near_zero():
     got = got_all[ms, ns]
     bad, d = within_tol(got, ref)
     rms = np.sqrt(np.mean(ref * ref))
-    say(f"  native c5: {int(bad.sum())} of {bad.size} over tolerance; max |d| {d.max():.3g}; rms|C| {rms:.3g}")
+    say(f"  native outlier workload: {int(bad.sum())} of {bad.size} over tolerance; max |d| {d.max():.3g}; rms|C| {rms:.3g}")
     assert np.all(np.abs(ref[bad]) < 0.05 * rms)
 
 
@@ -242,9 +242,9 @@ def _sign_case(R, M, kpr, N, cms, nbuf, density, seed):
 
 @pytest.mark.parametrize("precision", ["exact", "native"])
 @pytest.mark.parametrize("shape", [
-    (4, 1024, 1024, 2048, 256, 2, 0.06),      # the c2 geometry
-    (8, 64, 896, 2048, 8, 4, 0.03),           # the c4 geometry
-    (8, 1024, 1024, 8192, 512, 4, 0.03),      # the c5 geometry, first 1024 rows
+    (4, 1024, 1024, 2048, 256, 2, 0.06),      # the m1024_n2048_k4096 geometry
+    (8, 64, 896, 2048, 8, 4, 0.03),           # the skinny geometry
+    (8, 1024, 1024, 8192, 512, 4, 0.03),      # the 8192-column outlier geometry, first 1024 rows
 ])
 def test_integer_data_bit_exact(shape, precision):
     torch = torch_cuda()

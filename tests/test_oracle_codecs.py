@@ -181,7 +181,7 @@ def _torch_quantize(x32: np.ndarray):
     return q, s
 
 
-@pytest.mark.parametrize("name", ["c1", "c4"])
+@pytest.mark.parametrize("name", ["tiny_m128_n256_k512", "skinny_m64_n2048_k7168"])
 def test_quantizer_matches_torch_path(name):
     w = inputs.WORKLOADS[name]
     a32, b32 = inputs.fp32_operands(w)
@@ -212,7 +212,7 @@ def test_quantizer_outliers_and_edges_match_torch_path():
 
 
 def test_quantizer_invariants():
-    w = inputs.WORKLOADS["c1"]
+    w = inputs.WORKLOADS["tiny_m128_n256_k512"]
     a32, _ = inputs.fp32_operands(w)
     q, s = oracle.quantize_mxfp8(a32)
     assert not np.any((q & 0x7F) == 0x7F)              # never NaN

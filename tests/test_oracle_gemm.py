@@ -165,7 +165,7 @@ def test_oracle_all_ones_k256():
 
 
 def test_oracle_k_split_invariance():
-    w = inputs.WORKLOADS["c4"]
+    w = inputs.WORKLOADS["skinny_m64_n2048_k7168"]
     a32, b32 = inputs.fp32_operands(w)
     a32, b32 = a32[:8], b32[:16]
     qa, sa = oracle.quantize_mxfp8(a32)
@@ -179,7 +179,7 @@ def test_oracle_k_split_invariance():
 
 
 def test_oracle_matches_numpy_float64_matmul():
-    w = inputs.WORKLOADS["c1"]
+    w = inputs.WORKLOADS["tiny_m128_n256_k512"]
     a32, b32 = inputs.fp32_operands(w)
     qa, sa = oracle.quantize_mxfp8(a32)
     qb, sb = oracle.quantize_mxfp8(b32)
