@@ -62,6 +62,61 @@ def load_traffic(workload: str, sha: str):
     return d.get("hbm_bytes_per_launch")
 
 
+# Telemetry: a child process (started before this process touches the GPU)
+# polls amd-smi for the shader clocks of the XCDs and the socket power and
+# appends one JSON line per sample to a file.
+SAMPLER = r"""
+import json, os, subprocess, sys, time
+out, parent = sys.argv[1], int(sys.argv[2])
+while True:
+    try:
+        os.kill(parent, 0)
+    except OSError:
+        break
+    if os.path.exists(out + ".stop"):
+        break
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
+                           capture_output=True, text=True, timeout=10)
+        g = json.loads(r.stdout)["gpu_data"][0]
+        clk = [v["clk"]["value"] for k, v in g["clock"].items()
+               if k.startswith("gfx_") and isinstance(v.get("clk", {}).get("value"), (int, float))]
+        pw = g["power"]["socket_power"]["value"]
+        with open(out, "a") as f:
+            f.write(json.dumps({"t": time.time(), "gfx_mhz": clk, "power_w": pw}) + "\n")
+    except Exception:
+        time.sleep(0.5)
+    time.sleep(0.1)
+"""
+
+
+def start_sampler(path: str):
+    import shutil
+    import subprocess
+    if shutil.which("amd-smi") is None:
+        return None
+    for f in (path, path + ".stop"):
+        if os.path.exists(f):
+            os.remove(f)
+    return subprocess.Popen([sys.executable, "-c", SAMPLER, path, str(os.getpid())],
+                            stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+
+
+def read_samples(path: str, t0: float, t1: float):
+    if not os.path.exists(path):
+        return []
+    rows = []
+    with open(path) as f:
+        for line in f:
+            try:
+                d = json.loads(line)
+            except ValueError:
+                continue
+            if t0 <= d["t"] <= t1 and d["gfx_mhz"]:
+                rows.append(d)
+    return rows
+
+
 def cpu_baseline(w, target_s: float):
     """Time the CPU oracle (as it stands) on the first rows of C."""
     import numpy as np
@@ -97,6 +152,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--telemetry-seconds", type=float, default=2.0,
+                    help="sustained replays while amd-smi samples the shader clock (0: off)")
     ap.add_argument("--no-graph", action="store_true",
                     help="time steps issued on the stream (default: replays of one captured step)")
     ap.add_argument("--tile-cfg", type=int, default=-1)
@@ -124,6 +181,9 @@ def main():
               "method are simulated as segments in one GPU's memory, and no multi-GPU path is "
               "built.", file=sys.stderr)
         sys.exit(2)
+
+    tele_path = os.path.join("/tmp", f"mxgemm_bench_telemetry_{os.getpid()}.jsonl")
+    sampler = start_sampler(tele_path) if args.telemetry_seconds > 0 else None
 
     import torch
     import mxfp8_block_scaled_mxgemm_amd as pkg
@@ -221,6 +281,29 @@ def main():
         sms, _ = timed(False)
         stream_ms = statistics.mean(sms)
         log(f"[bench] stream-issued: mean {stream_ms:.4f} ms")
+
+    # ---- telemetry window: sustained steps while the sampler runs --------
+    telemetry = None
+    if sampler is not None:
+        t0 = time.time()
+        while time.time() - t0 < args.telemetry_seconds:
+            for _ in range(8):
+                if graph is not None:
+                    graph.replay()
+                else:
+                    step()
+            torch.cuda.synchronize()
+        t1 = time.time()
+        rows = read_samples(tele_path, t0, t1)
+        if rows:
+            mhz = [statistics.mean(r["gfx_mhz"]) for r in rows]
+            telemetry = {"samples": len(rows), "shader_clock_mhz_median": round(statistics.median(mhz), 1),
+                         "shader_clock_mhz_min": round(min(mhz), 1),
+                         "socket_power_w_median": round(statistics.median(r["power_w"] for r in rows), 1),
+                         "source": "amd-smi metric --clock --power, mean over XCDs, during "
+                                   f"{t1 - t0:.1f} s of back-to-back steps (no flush)"}
+            log(f"[bench] telemetry: {telemetry}")
+    if graph is not None:
         del graph
 
     # ---- per-kernel durations (HIP events around each launch) -----------
@@ -253,6 +336,16 @@ def main():
     log(f"[bench] kernels: gemm {gemm_ms_per_launch * 1e3:.2f} us/launch x{plan['windows']}, "
         f"stage {stage_ms_per_launch * 1e3:.2f} us/launch")
 
+    if sampler is not None:
+        open(tele_path + ".stop", "w").close()
+        try:
+            sampler.wait(timeout=15)
+        except Exception:
+            sampler.kill()
+        for f in (tele_path, tele_path + ".stop"):
+            if os.path.exists(f):
+                os.remove(f)
+
     sha = kernel_source_sha()
     traffic = load_traffic(args.config, sha)
 
@@ -284,6 +377,10 @@ def main():
                   + ", HIP events per step" + (", 512 MiB cache flush before each step"
                                                  if not args.no_flush else ", warm caches")),
         "stream_issued_ms_per_step": round(stream_ms, 5) if stream_ms is not None else None,
+        "ms_per_step_median": round(statistics.median(ms), 5),
+        "ms_per_step_min": round(min(ms), 5),
+        "ms_per_step_p90": round(sorted(ms)[min(len(ms) - 1, int(0.9 * len(ms)))], 5),
+        "telemetry": telemetry,
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "precision": args.precision,
         "roofline": {
@@ -294,6 +391,10 @@ def main():
             "peak": roof_peak,
             "unit": roof_unit,
             "frac": round(achieved / roof_peak, 4),
+            # the same fraction against the peak at the shader clock measured
+            # while the kernel ran (MFMA bound only)
+            "frac_at_measured_clock": (round(achieved / (roof_peak * telemetry["shader_clock_mhz_median"] / 2400.0), 4)
+                                       if telemetry and not hbm_bound else None),
             "gemm_tflops": round(flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12, 3),
             "frac_of_mxfp8_peak": round(flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
                                         / PEAK_FP8_TFLOPS, 4),

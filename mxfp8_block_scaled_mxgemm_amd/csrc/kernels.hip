@@ -640,7 +640,11 @@ mxgemm_kernel(GemmArgs p)
                 // B use the same K assignment, so every product pairs
                 // correctly; products are exact in the MFMA and summed with
                 // FP32-grade precision.
+                // All four blocks' codes are read first: one LDS round
+                // trip per K-step (these small tiles have few MFMAs to hide
+                // latency behind).
                 uint32_t sa_w[GA], sb_w[GB];
+                u32x2 rb[4][GB], ra[4][GA];
 #pragma unroll
                 for (int g = 0; g < GB; ++g)
                     sb_w[g] = *reinterpret_cast<const uint32_t*>(psb + g * MW * 4);
@@ -650,29 +654,27 @@ mxgemm_kernel(GemmArgs p)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int lane_off = chunk(2 * j + (lq >> 1)) + (lq & 1) * 8;
-                    u32x2 rb[GB], ra[GA];
 #pragma unroll
                     for (int g = 0; g < GB; ++g)
-                        rb[g] = *reinterpret_cast<const u32x2*>(pb + g * MW * kBK + lane_off);
+                        rb[j][g] = *reinterpret_cast<const u32x2*>(pb + g * MW * kBK + lane_off);
 #pragma unroll
                     for (int i = 0; i < GA; ++i)
-                        ra[i] = *reinterpret_cast<const u32x2*>(pa + i * MW * kBK + lane_off);
-                    v8bf bb[GB];
+                        ra[j][i] = *reinterpret_cast<const u32x2*>(pa + i * MW * kBK + lane_off);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    v8bf bb[GB], ab[GA];
 #pragma unroll
                     for (int g = 0; g < GB; ++g)
-                        bb[g] = fp8x8_to_bf16(rb[g], e8m0_to_f32(sb_w[g] >> (8 * j)));
-                    v8bf ab[2];
-                    ab[0] = fp8x8_to_bf16(ra[0], e8m0_to_f32(sa_w[0] >> (8 * j)));
+                        bb[g] = fp8x8_to_bf16(rb[j][g], e8m0_to_f32(sb_w[g] >> (8 * j)));
 #pragma unroll
-                    for (int i = 0; i < GA; ++i) {
-                        const int cur = i & 1;
+                    for (int i = 0; i < GA; ++i)
+                        ab[i] = fp8x8_to_bf16(ra[j][i], e8m0_to_f32(sa_w[i] >> (8 * j)));
+#pragma unroll
+                    for (int i = 0; i < GA; ++i)
 #pragma unroll
                         for (int g = 0; g < GB; ++g)
-                            acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[g], ab[cur], acc[i][g], 0, 0, 0);
-                        if (i + 1 < GA)
-                            ab[cur ^ 1] = fp8x8_to_bf16(ra[i + 1], e8m0_to_f32(sa_w[i + 1] >> (8 * j)));
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
+                            acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[g], ab[i], acc[i][g], 0, 0, 0);
                 }
             }
 

@@ -91,8 +91,8 @@ double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int s
     const int64_t rounds = ceil_div(work, cap);
     const double flops = 2.0 * t.tile_m * t.tile_n * (double)(K / split);
     const double peak = exact ? 4096.0 : 8192.0;   // FLOP per clock per CU
-    // under a full MFMA load the shader clock settles near 1.5 GHz, so
-    // compute takes ~1.6x its 2.4 GHz cycle count in wall time
+    // under a full MFMA load the part sits at its power cap: measured
+    // MFMA work takes ~1.6x its 2.4 GHz cycle count in wall time
     const double compute = flops / (peak * t.rel_rate) * t.blocks_per_cu * 1.6;
     const int64_t stages = ceil_div(K / split / 128, t.steps_per_stage);
     const double copy = (double)stages * 4400.0;
