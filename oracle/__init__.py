@@ -57,11 +57,17 @@ def _load():
         lib.oracle_bf16_from_double.restype = ctypes.c_uint16
         lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
         lib.oracle_quantize_mxfp8.argtypes = [_f32p, _i64, _i64, _u8p, _u8p]
-        lib.oracle_mxgemm_seg.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _i64, _u16p]
+        lib.oracle_quantize_mx.argtypes = [_f32p, _i64, _i64, _u8p, _u8p, ctypes.c_int]
+        lib.oracle_mxgemm_seg.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _i64, _u16p,
+                                          ctypes.c_int, ctypes.c_int]
         lib.oracle_mxgemm_seg_entries.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _i64,
-                                                  _i64p, _i64p, _i64, _u16p, _f64p]
+                                                  _i64p, _i64p, _i64, _u16p, _f64p,
+                                                  ctypes.c_int, ctypes.c_int]
         lib.oracle_mxgemm_seg_rows.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _i64,
-                                               _i64, _i64, _u16p]
+                                               _i64, _i64, _u16p, ctypes.c_int, ctypes.c_int]
+        lib.oracle_e5m2_encode_array.argtypes = [_f64p, _i64, _u8p]
+        lib.oracle_e5m2_value_array.argtypes = [_u8p, _i64, _f64p]
+        lib.oracle_e8m0_exponent_e5m2_array.argtypes = [_f64p, _i64, _i32p]
         lib.oracle_e4m3_encode_array.argtypes = [_f64p, _i64, _u8p]
         lib.oracle_e4m3_value_array.argtypes = [_u8p, _i64, _f64p]
         lib.oracle_e8m0_exponent_array.argtypes = [_f64p, _i64, _i32p]
@@ -100,6 +106,39 @@ def e8m0_exponent(amax) -> np.ndarray:
     return out.reshape(np.shape(amax))
 
 
+# format codes of the FP8 operands
+E4M3, E5M2 = 0, 1
+
+
+def _fmt(f) -> int:
+    if f in (E4M3, "e4m3"):
+        return E4M3
+    if f in (E5M2, "e5m2"):
+        return E5M2
+    raise ValueError(f"unknown FP8 format {f!r}")
+
+
+def e5m2_value(codes) -> np.ndarray:
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8).ravel())
+    out = np.empty(c.size, dtype=np.float64)
+    _load().oracle_e5m2_value_array(_p(c, _u8p), c.size, _p(out, _f64p))
+    return out.reshape(np.shape(codes))
+
+
+def e5m2_encode(values) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(values, dtype=np.float64).ravel())
+    out = np.empty(v.size, dtype=np.uint8)
+    _load().oracle_e5m2_encode_array(_p(v, _f64p), v.size, _p(out, _u8p))
+    return out.reshape(np.shape(values))
+
+
+def e8m0_exponent_e5m2(amax) -> np.ndarray:
+    v = np.ascontiguousarray(np.asarray(amax, dtype=np.float64).ravel())
+    out = np.empty(v.size, dtype=np.int32)
+    _load().oracle_e8m0_exponent_e5m2_array(_p(v, _f64p), v.size, _p(out, _i32p))
+    return out.reshape(np.shape(amax))
+
+
 def bf16_from_double(values) -> np.ndarray:
     v = np.ascontiguousarray(np.asarray(values, dtype=np.float64).ravel())
     out = np.empty(v.size, dtype=np.uint16)
@@ -107,16 +146,16 @@ def bf16_from_double(values) -> np.ndarray:
     return out.reshape(np.shape(values))
 
 
-def quantize_mxfp8(x) -> tuple:
+def quantize_mxfp8(x, fmt=E4M3) -> tuple:
     """``x`` float32 ``[rows, cols]`` (cols % 32 == 0) -> (codes uint8
-    ``[rows, cols]``, scale bytes uint8 ``[rows, cols/32]``)."""
+    ``[rows, cols]`` of format ``fmt``, scale bytes uint8 ``[rows, cols/32]``)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     rows, cols = x.shape
     if cols % 32:
         raise ValueError("cols must be a multiple of 32")
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty((rows, cols // 32), dtype=np.uint8)
-    _load().oracle_quantize_mxfp8(_p(x, _f32p), rows, cols, _p(q, _u8p), _p(s, _u8p))
+    _load().oracle_quantize_mx(_p(x, _f32p), rows, cols, _p(q, _u8p), _p(s, _u8p), _fmt(fmt))
     return q, s
 
 
@@ -134,19 +173,21 @@ def _check(a_seg, sa_seg, b, sb):
     return a_seg, sa_seg, b, sb, R, M, kpr, N
 
 
-def mxgemm_seg(a_seg, sa_seg, b, sb) -> np.ndarray:
+def mxgemm_seg(a_seg, sa_seg, b, sb, fmt_a=E4M3, fmt_b=E4M3) -> np.ndarray:
     """Full C ``[M, N]`` as bfloat16 bit patterns (uint16).
 
     ``a_seg`` [R, M, kPerRank] codes, ``sa_seg`` [R, M, kPerRank/32] scale
-    bytes, ``b`` [N, K] codes, ``sb`` [N, K/32] scale bytes."""
+    bytes, ``b`` [N, K] codes, ``sb`` [N, K/32] scale bytes; A codes of
+    format ``fmt_a``, B codes of ``fmt_b``."""
     a_seg, sa_seg, b, sb, R, M, kpr, N = _check(a_seg, sa_seg, b, sb)
     c = np.empty((M, N), dtype=np.uint16)
     _load().oracle_mxgemm_seg(_p(a_seg, _u8p), _p(sa_seg, _u8p), _p(b, _u8p), _p(sb, _u8p),
-                              R, M, kpr, N, _p(c, _u16p))
+                              R, M, kpr, N, _p(c, _u16p), _fmt(fmt_a), _fmt(fmt_b))
     return c
 
 
-def mxgemm_seg_entries(a_seg, sa_seg, b, sb, ms, ns, want_exact: bool = False):
+def mxgemm_seg_entries(a_seg, sa_seg, b, sb, ms, ns, want_exact: bool = False,
+                       fmt_a=E4M3, fmt_b=E4M3):
     """C at the listed (ms[i], ns[i]) as bfloat16 bits; optionally also the
     unrounded double sums."""
     a_seg, sa_seg, b, sb, R, M, kpr, N = _check(a_seg, sa_seg, b, sb)
@@ -161,18 +202,19 @@ def mxgemm_seg_entries(a_seg, sa_seg, b, sb, ms, ns, want_exact: bool = False):
     _load().oracle_mxgemm_seg_entries(_p(a_seg, _u8p), _p(sa_seg, _u8p), _p(b, _u8p),
                                       _p(sb, _u8p), R, M, kpr, N, _p(ms, _i64p), _p(ns, _i64p),
                                       ms.size, _p(c, _u16p),
-                                      _p(ex, _f64p) if want_exact else None)
+                                      _p(ex, _f64p) if want_exact else None,
+                                      _fmt(fmt_a), _fmt(fmt_b))
     return (c, ex) if want_exact else c
 
 
-def mxgemm_seg_rows(a_seg, sa_seg, b, sb, m0: int, m1: int) -> np.ndarray:
+def mxgemm_seg_rows(a_seg, sa_seg, b, sb, m0: int, m1: int, fmt_a=E4M3, fmt_b=E4M3) -> np.ndarray:
     """Rows ``[m0, m1)`` of C as bfloat16 bits."""
     a_seg, sa_seg, b, sb, R, M, kpr, N = _check(a_seg, sa_seg, b, sb)
     if not (0 <= m0 <= m1 <= M):
         raise ValueError("row range out of bounds")
     c = np.empty((m1 - m0, N), dtype=np.uint16)
     _load().oracle_mxgemm_seg_rows(_p(a_seg, _u8p), _p(sa_seg, _u8p), _p(b, _u8p), _p(sb, _u8p),
-                                   R, M, kpr, N, m0, m1, _p(c, _u16p))
+                                   R, M, kpr, N, m0, m1, _p(c, _u16p), _fmt(fmt_a), _fmt(fmt_b))
     return c
 
 

@@ -36,6 +36,14 @@
  *    448 * 2^e >= amax (that is 2^ceil(log2(amax/448))), clamped to
  *    [-127, 127], amax = 0 giving -127; the scale byte is e + 127 and each
  *    element is encoded as e4m3_rne(x * 2^-e), keeping the sign of zero.
+ *
+ * The other FP8 operand formats (all_to_all_matmul_impl.h, the sibling
+ * kernel entries E5M2E5M2, E4M3E5M2 and E5M2E4M3): either operand may be
+ * E5M2 instead, the OCP OFP8 format with bias 15, IEEE-style infinities
+ * (0x7C / 0xFC) and NaNs (0x7D-0x7F, 0xFD-0xFF), largest finite 57344 and
+ * subnormal step 2^-16.  Its quantiser uses 57344 in place of 448 and
+ * saturates to 57344 (MX conversions saturate).  Format codes below: 0 =
+ * E4M3, 1 = E5M2.
  */
 #include <math.h>
 #include <stdint.h>
@@ -94,6 +102,63 @@ uint8_t oracle_e4m3_encode(double v)
     }
 }
 
+/* ---------------------------------------------------------------- E5M2 --- */
+
+/* Value of an E5M2 code (infinities at 0x7C / 0xFC, NaN above them). */
+double oracle_e5m2_value(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int expo = (code >> 2) & 0x1F;
+    int mant = code & 0x3;
+    double v;
+    if (expo == 0x1F)
+        return mant == 0 ? (sign ? -INFINITY : INFINITY) : NAN;
+    if (expo == 0)
+        v = ldexp((double)mant, -16);               /* mant/4 * 2^(1-15) */
+    else
+        v = ldexp(1.0 + (double)mant / 4.0, expo - 15);
+    return sign ? -v : v;
+}
+
+/* E5M2 code of v, round-to-nearest-even; magnitudes above 57344 after
+ * rounding (infinities included) saturate to 57344, NaN gives 0x7F. */
+uint8_t oracle_e5m2_encode(double v)
+{
+    uint8_t sign;
+    double a;
+    if (isnan(v))
+        return 0x7F;
+    sign = signbit(v) ? 0x80 : 0x00;
+    a = fabs(v);
+    if (isinf(a))
+        return (uint8_t)(sign | 0x7B);
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: multiples of 2^-16; q == 4 is the smallest
+         * normal, whose code is also 4 */
+        double q = rint(ldexp(a, 16));
+        return (uint8_t)(sign | (uint8_t)q);
+    } else {
+        int E;
+        double f = frexp(a, &E);        /* a = f * 2^E, f in [0.5, 1) */
+        int e = E - 1;                  /* a in [2^e, 2^(e+1)) */
+        double q = rint(ldexp(f, 3));   /* a / 2^(e-2), in [4, 8] */
+        int iq = (int)q;
+        if (iq == 8) {
+            iq = 4;
+            e += 1;
+        }
+        if (e > 15 || (e == 15 && iq > 7))
+            return (uint8_t)(sign | 0x7B);          /* saturate at 57344 */
+        return (uint8_t)(sign | (uint8_t)(((e + 15) << 2) | (iq - 4)));
+    }
+}
+
+/* Value of a code of format fmt (0 = E4M3, 1 = E5M2). */
+double oracle_fp8_value(uint8_t code, int fmt)
+{
+    return fmt ? oracle_e5m2_value(code) : oracle_e4m3_value(code);
+}
+
 /* --------------------------------------------------------------- E8M0 --- */
 
 /* Smallest integer e with 448 * 2^e >= amax, clamped to [-127, 127]. */
@@ -113,8 +178,53 @@ int oracle_e8m0_exponent(double amax)
     return e;
 }
 
+/* Smallest integer e with 57344 * 2^e >= amax (the E5M2 largest finite),
+ * clamped to [-127, 127]. */
+int oracle_e8m0_exponent_e5m2(double amax)
+{
+    int E, e;
+    double f;
+    if (!(amax > 0.0))
+        return -127;
+    f = frexp(amax, &E);
+    /* 57344 = 0.875 * 2^16: amax <= 57344 * 2^e <=> f * 2^E <= 0.875 * 2^(e+16) */
+    e = (f <= 0.875) ? E - 16 : E - 15;
+    if (e < -127)
+        e = -127;
+    if (e > 127)
+        e = 127;
+    return e;
+}
+
 /* Quantise a row-major [rows][cols] float32 matrix (cols % 32 == 0) into
- * codes [rows][cols] and scale bytes [rows][cols/32]. */
+ * codes [rows][cols] of format fmt and scale bytes [rows][cols/32]. */
+void oracle_quantize_mx(const float* x, int64_t rows, int64_t cols,
+                        uint8_t* q, uint8_t* s, int fmt)
+{
+    int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* blk = x + i * cols + b * 32;
+            double amax = 0.0;
+            int e, j;
+            for (j = 0; j < 32; ++j) {
+                double a = fabs((double)blk[j]);
+                if (a > amax)
+                    amax = a;
+            }
+            e = fmt ? oracle_e8m0_exponent_e5m2(amax) : oracle_e8m0_exponent(amax);
+            s[i * nb + b] = (uint8_t)(e + 127);
+            for (j = 0; j < 32; ++j) {
+                double y = ldexp((double)blk[j], -e);
+                q[i * cols + b * 32 + j] = fmt ? oracle_e5m2_encode(y) : oracle_e4m3_encode(y);
+            }
+        }
+    }
+}
+
+/* Quantise a row-major [rows][cols] float32 matrix (cols % 32 == 0) into
+ * E4M3 codes [rows][cols] and scale bytes [rows][cols/32]. */
 void oracle_quantize_mxfp8(const float* x, int64_t rows, int64_t cols,
                            uint8_t* q, uint8_t* s)
 {
@@ -181,7 +291,7 @@ static double e8m0_value(uint8_t s)
 }
 
 /* One output element, summed in double, r ascending then k ascending. */
-static double dot_entry(const double* lut,
+static double dot_entry(const double* lut_a, const double* lut_b,
                         const uint8_t* a_seg, const uint8_t* sa_seg,
                         const uint8_t* b, const uint8_t* sb,
                         int64_t R, int64_t M, int64_t kpr, int64_t m, int64_t n)
@@ -194,35 +304,36 @@ static double dot_entry(const double* lut,
         const uint8_t* asrow = sa_seg + (r * M + m) * nbs;
         for (int64_t k = 0; k < kpr; ++k) {
             int64_t kg = r * kpr + k;
-            double av = lut[arow[k]] * e8m0_value(asrow[k / 32]);
-            double bv = lut[b[n * K + kg]] * e8m0_value(sb[n * nbk + kg / 32]);
+            double av = lut_a[arow[k]] * e8m0_value(asrow[k / 32]);
+            double bv = lut_b[b[n * K + kg]] * e8m0_value(sb[n * nbk + kg / 32]);
             acc += av * bv;
         }
     }
     return acc;
 }
 
-static void fill_lut(double* lut)
+static void fill_lut(double* lut, int fmt)
 {
     for (int c = 0; c < 256; ++c)
-        lut[c] = oracle_e4m3_value((uint8_t)c);
+        lut[c] = oracle_fp8_value((uint8_t)c, fmt);
 }
 
-/* Full C [M][N] as bfloat16 bits.
+/* Full C [M][N] as bfloat16 bits; A codes of format fmt_a, B of fmt_b.
  *   a_seg  [R][M][kpr]      sa_seg [R][M][kpr/32]
  *   b      [N][R*kpr]       sb     [N][R*kpr/32]          */
 void oracle_mxgemm_seg(const uint8_t* a_seg, const uint8_t* sa_seg,
                        const uint8_t* b, const uint8_t* sb,
                        int64_t R, int64_t M, int64_t kpr, int64_t N,
-                       uint16_t* c)
+                       uint16_t* c, int fmt_a, int fmt_b)
 {
-    double lut[256];
-    fill_lut(lut);
+    double lut_a[256], lut_b[256];
+    fill_lut(lut_a, fmt_a);
+    fill_lut(lut_b, fmt_b);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
             c[m * N + n] = oracle_bf16_from_double(
-                dot_entry(lut, a_seg, sa_seg, b, sb, R, M, kpr, m, n));
+                dot_entry(lut_a, lut_b, a_seg, sa_seg, b, sb, R, M, kpr, m, n));
 }
 
 /* Selected entries only: c[i] = C[ms[i], ns[i]] as bfloat16 bits, and, if
@@ -231,14 +342,15 @@ void oracle_mxgemm_seg_entries(const uint8_t* a_seg, const uint8_t* sa_seg,
                                const uint8_t* b, const uint8_t* sb,
                                int64_t R, int64_t M, int64_t kpr, int64_t N,
                                const int64_t* ms, const int64_t* ns, int64_t count,
-                               uint16_t* c, double* exact)
+                               uint16_t* c, double* exact, int fmt_a, int fmt_b)
 {
-    double lut[256];
+    double lut_a[256], lut_b[256];
     (void)N;
-    fill_lut(lut);
+    fill_lut(lut_a, fmt_a);
+    fill_lut(lut_b, fmt_b);
 #pragma omp parallel for schedule(dynamic, 64)
     for (int64_t i = 0; i < count; ++i) {
-        double v = dot_entry(lut, a_seg, sa_seg, b, sb, R, M, kpr, ms[i], ns[i]);
+        double v = dot_entry(lut_a, lut_b, a_seg, sa_seg, b, sb, R, M, kpr, ms[i], ns[i]);
         c[i] = oracle_bf16_from_double(v);
         if (exact)
             exact[i] = v;
@@ -249,15 +361,16 @@ void oracle_mxgemm_seg_entries(const uint8_t* a_seg, const uint8_t* sa_seg,
 void oracle_mxgemm_seg_rows(const uint8_t* a_seg, const uint8_t* sa_seg,
                             const uint8_t* b, const uint8_t* sb,
                             int64_t R, int64_t M, int64_t kpr, int64_t N,
-                            int64_t m0, int64_t m1, uint16_t* c)
+                            int64_t m0, int64_t m1, uint16_t* c, int fmt_a, int fmt_b)
 {
-    double lut[256];
-    fill_lut(lut);
+    double lut_a[256], lut_b[256];
+    fill_lut(lut_a, fmt_a);
+    fill_lut(lut_b, fmt_b);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t m = m0; m < m1; ++m)
         for (int64_t n = 0; n < N; ++n)
             c[(m - m0) * N + n] = oracle_bf16_from_double(
-                dot_entry(lut, a_seg, sa_seg, b, sb, R, M, kpr, m, n));
+                dot_entry(lut_a, lut_b, a_seg, sa_seg, b, sb, R, M, kpr, m, n));
 }
 
 /* Elementwise helpers exposed for the pins. */
@@ -278,6 +391,25 @@ void oracle_e8m0_exponent_array(const double* amax, int64_t n, int32_t* out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = oracle_e8m0_exponent(amax[i]);
+}
+
+void oracle_e5m2_encode_array(const double* v, int64_t n, uint8_t* out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e5m2_encode(v[i]);
+}
+
+void oracle_e5m2_value_array(const uint8_t* codes, int64_t n, double* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e5m2_value(codes[i]);
+}
+
+void oracle_e8m0_exponent_e5m2_array(const double* amax, int64_t n, int32_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_e8m0_exponent_e5m2(amax[i]);
 }
 
 void oracle_bf16_from_double_array(const double* v, int64_t n, uint16_t* out)
