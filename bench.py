@@ -161,6 +161,10 @@ def main():
     ap.add_argument("--window", type=int, default=-1)
     ap.add_argument("--precision", choices=["exact", "native"], default="exact",
                     help="GEMM arithmetic (default exact: parity-green on every workload)")
+    ap.add_argument("--a-format", choices=["e4m3", "e5m2"], default="e4m3",
+                    help="FP8 format of the A codes")
+    ap.add_argument("--b-format", choices=["e4m3", "e5m2"], default="e4m3",
+                    help="FP8 format of the B codes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy 256 MiB device-to-device three times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -201,8 +205,8 @@ def main():
     a_d = torch.from_numpy(a32).to(dev)
     b_d = torch.from_numpy(b32).to(dev)
     del a32, b32
-    a_q, a_s = pkg.quantize_segments(a_d, w.R)
-    b_q, b_s = pkg.quantize_mxfp8(b_d)
+    a_q, a_s = pkg.quantize_segments(a_d, w.R, fmt=args.a_format)
+    b_q, b_s = pkg.quantize_mxfp8(b_d, fmt=args.b_format)
     del a_d, b_d
     c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
@@ -210,9 +214,11 @@ def main():
 
     opts = None
     prec = pkg.PRECISION_EXACT if args.precision == "exact" else pkg.PRECISION_NATIVE
-    if args.tile_cfg >= 0 or args.split > 0 or args.window > 0 or prec != pkg.PRECISION_EXACT:
+    fmts = (args.a_format, args.b_format)
+    if (args.tile_cfg >= 0 or args.split > 0 or args.window > 0 or prec != pkg.PRECISION_EXACT
+            or fmts != ("e4m3", "e4m3")):
         opts = pkg.options(tile_cfg=args.tile_cfg, split=args.split, chunks_per_window=args.window,
-                           precision=prec)
+                           precision=prec, a_format=args.a_format, b_format=args.b_format)
     g = pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts)
     plan = g.plan.as_dict()
     log(f"[bench] plan: {plan}")
@@ -366,7 +372,8 @@ def main():
         "config": {"workload": f"{args.config}: {w.describe()}, "
                                f"N(0,{w.sigma:g})" + (f" with {w.outlier_frac:.0%} of entries "
                                f"x{w.outlier_mul:g}" if w.outlier_frac else "") +
-                               f", seed {w.seed}; MXFP8 E4M3 + E8M0/32 in, bfloat16 out",
+                               f", seed {w.seed}; MXFP8 A {args.a_format.upper()}, "
+                               f"B {args.b_format.upper()} + E8M0/32 in, bfloat16 out",
                    "flop_per_step": w.flops,
                    "algorithmic_bytes_per_step": w.algorithmic_bytes,
                    "plan": {k: plan[k] for k in ("tile_m", "tile_n", "split", "chunks_per_window",

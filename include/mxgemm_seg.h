@@ -60,6 +60,16 @@ typedef struct mxgemm_seg* mxgemm_seg_t;
  *    small. */
 enum { MXGEMM_PRECISION_EXACT = 0, MXGEMM_PRECISION_NATIVE = 1 };
 
+/* FP8 formats of the A and B codes.  The pages ship four entries of the
+ * same operator, one per (A, B) pair of E4M3 (OCP "FN") and E5M2 (OCP,
+ * bias 15, infinities and NaNs, largest finite 57344):
+ * all_to_all_matmul_impl.h, AllToAllQuantMatmulKernelE4M3E4M3, ...E5M2E5M2,
+ * ...E4M3E5M2 and ...E5M2E4M3.  Scales are E8M0 per 32 K-elements in every
+ * case.  Exact mode converts either format to bfloat16 exactly (E5M2 codes
+ * need a scale byte >= 10 to stay on the bfloat16 grid, E4M3 codes >= 3);
+ * native mode passes the formats to the scaled MFMA. */
+enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
+
 /* Plan chosen for a problem: filled by mxgemm_seg_plan (host only, no GPU)
  * and by mxgemm_seg_get_plan for a live handle. */
 typedef struct mxgemm_seg_plan {
@@ -79,6 +89,8 @@ typedef struct mxgemm_seg_plan {
     int32_t group_n;           /* N-tiles per zigzag group                  */
     int32_t num_cus;
     int32_t precision;         /* MXGEMM_PRECISION_*                        */
+    int32_t a_format;          /* MXGEMM_FMT_* of the A codes               */
+    int32_t b_format;          /* MXGEMM_FMT_* of the B codes               */
     int32_t reserved;
     int64_t slot_bytes;        /* one staging buffer: R*commMSize*kPerRank  */
     int64_t scale_slot_bytes;  /* its scales: R*commMSize*kPerRank/32       */
@@ -91,6 +103,8 @@ typedef struct mxgemm_seg_options {
     int32_t split;             /* force S (must divide rank_size)           */
     int32_t chunks_per_window; /* force W (must divide buffer_count)        */
     int32_t precision;         /* MXGEMM_PRECISION_* (-1 = EXACT)           */
+    int32_t a_format;          /* MXGEMM_FMT_* of A (-1 = E4M3)             */
+    int32_t b_format;          /* MXGEMM_FMT_* of B (-1 = E4M3)             */
 } mxgemm_seg_options_t;
 
 /*
@@ -192,6 +206,17 @@ int mxgemm_seg_decode(const mxgemm_seg_plan_t* plan, int64_t rows, int32_t w, in
  */
 int mxgemm_quantize_mxfp8(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
                           uint8_t* q, int64_t ld_q, uint8_t* s, int64_t ld_s, void* stream);
+
+/*
+ * As mxgemm_quantize_mxfp8 for codes of `format` (MXGEMM_FMT_*).  For E5M2
+ * the rule uses its largest finite value: e = the smallest integer with
+ * 57344 * 2^e >= amax, clamped to [-127, 127], and codes are E5M2
+ * round-to-nearest-even of x * 2^-e, saturating at 57344 (MX conversions
+ * saturate).  Errors: EINVAL (also for an unknown format), EHIP.
+ */
+int mxgemm_quantize_mx(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
+                       uint8_t* q, int64_t ld_q, uint8_t* s, int64_t ld_s, int32_t format,
+                       void* stream);
 
 /*
  * Kernel timing for measurement.  While enabled, run() brackets every GEMM

@@ -23,8 +23,8 @@ _NAMES = {MXGEMM_EINVAL: "EINVAL", MXGEMM_ENOMEM: "ENOMEM", MXGEMM_EHIP: "EHIP",
 EXPORTED = [
     "mxgemm_seg_create", "mxgemm_seg_create_ex", "mxgemm_seg_run", "mxgemm_seg_destroy",
     "mxgemm_seg_last_error", "mxgemm_seg_get_plan", "mxgemm_seg_plan", "mxgemm_seg_decode",
-    "mxgemm_quantize_mxfp8", "mxgemm_seg_set_profiling", "mxgemm_seg_kernel_times",
-    "mxgemm_seg_version",
+    "mxgemm_quantize_mxfp8", "mxgemm_quantize_mx", "mxgemm_seg_set_profiling",
+    "mxgemm_seg_kernel_times", "mxgemm_seg_version",
 ]
 
 
@@ -44,7 +44,8 @@ class Plan(ctypes.Structure):
         ("tile_cfg", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
         ("split", ctypes.c_int32), ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
         ("work_items", ctypes.c_int32), ("grid", ctypes.c_int32), ("group_n", ctypes.c_int32),
-        ("num_cus", ctypes.c_int32), ("precision", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32), ("precision", ctypes.c_int32),
+        ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("slot_bytes", ctypes.c_int64), ("scale_slot_bytes", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
     ]
@@ -55,16 +56,29 @@ class Plan(ctypes.Structure):
 
 PRECISION_EXACT = 0
 PRECISION_NATIVE = 1
+FMT_E4M3 = 0
+FMT_E5M2 = 1
+
+
+def _fmt(f) -> int:
+    """Format code of ``f`` (a code, "e4m3"/"e5m2", or -1/None for the default)."""
+    if f is None or f == -1:
+        return -1
+    if isinstance(f, str):
+        return {"e4m3": FMT_E4M3, "e5m2": FMT_E5M2}[f.lower()]
+    return int(f)
 
 
 class Options(ctypes.Structure):
     _fields_ = [("tile_cfg", ctypes.c_int32), ("split", ctypes.c_int32),
                 ("chunks_per_window", ctypes.c_int32),
-                ("precision", ctypes.c_int32)]
+                ("precision", ctypes.c_int32),
+                ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32)]
 
 
-def options(tile_cfg=-1, split=-1, chunks_per_window=-1, precision=-1) -> Options:
-    return Options(tile_cfg, split, chunks_per_window, precision)
+def options(tile_cfg=-1, split=-1, chunks_per_window=-1, precision=-1, a_format=-1,
+            b_format=-1) -> Options:
+    return Options(tile_cfg, split, chunks_per_window, precision, _fmt(a_format), _fmt(b_format))
 
 
 _lib = None
@@ -93,12 +107,14 @@ def load():
     p32 = ctypes.POINTER(i32)
     lib.mxgemm_seg_decode.argtypes = [ctypes.POINTER(Plan), i64, i32, i32, p32, p32, p32, p32]
     lib.mxgemm_quantize_mxfp8.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
+    lib.mxgemm_quantize_mx.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, i32, vp]
     lib.mxgemm_seg_set_profiling.argtypes = [vp, i32]
     lib.mxgemm_seg_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), p32,
                                             ctypes.POINTER(ctypes.c_double), p32]
     for name in ("mxgemm_seg_create", "mxgemm_seg_create_ex", "mxgemm_seg_run",
                  "mxgemm_seg_destroy", "mxgemm_seg_get_plan", "mxgemm_seg_plan",
-                 "mxgemm_seg_decode", "mxgemm_quantize_mxfp8", "mxgemm_seg_set_profiling",
+                 "mxgemm_seg_decode", "mxgemm_quantize_mxfp8", "mxgemm_quantize_mx",
+                 "mxgemm_seg_set_profiling",
                  "mxgemm_seg_kernel_times"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -223,10 +239,11 @@ class SegGemm:
             pass
 
 
-def quantize_mxfp8(x, q=None, s=None, stream=None):
+def quantize_mxfp8(x, q=None, s=None, stream=None, fmt=FMT_E4M3):
     """GPU MXFP8 quantiser: float32 device tensor [rows, cols] (cols % 32 == 0,
-    last dim contiguous) -> (uint8 codes [rows, cols], uint8 scales
-    [rows, cols/32]).  Outputs may be given (views with unit last stride)."""
+    last dim contiguous) -> (uint8 codes [rows, cols] of format ``fmt``,
+    uint8 scales [rows, cols/32]).  Outputs may be given (views with unit
+    last stride)."""
     import torch
     if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D float32 tensor with contiguous rows")
@@ -238,14 +255,14 @@ def quantize_mxfp8(x, q=None, s=None, stream=None):
     if q.stride(1) != 1 or s.stride(1) != 1 or tuple(q.shape) != (rows, cols) \
             or tuple(s.shape) != (rows, cols // 32):
         raise ValueError("bad output tensors")
-    check(load().mxgemm_quantize_mxfp8(ctypes.c_void_p(x.data_ptr()), rows, cols, x.stride(0),
-                                       ctypes.c_void_p(q.data_ptr()), q.stride(0),
-                                       ctypes.c_void_p(s.data_ptr()), s.stride(0),
-                                       _stream_ptr(stream)))
+    check(load().mxgemm_quantize_mx(ctypes.c_void_p(x.data_ptr()), rows, cols, x.stride(0),
+                                    ctypes.c_void_p(q.data_ptr()), q.stride(0),
+                                    ctypes.c_void_p(s.data_ptr()), s.stride(0),
+                                    max(0, _fmt(fmt)), _stream_ptr(stream)))
     return q, s
 
 
-def quantize_segments(a32, R: int, stream=None):
+def quantize_segments(a32, R: int, stream=None, fmt=FMT_E4M3):
     """Quantise float32 A [M, K] straight into the segment layout:
     codes [R, M, K/R] and scales [R, M, K/(32R)] (one quantiser launch per
     segment, each reading a column slice of A)."""
@@ -255,5 +272,5 @@ def quantize_segments(a32, R: int, stream=None):
     q = torch.empty((R, M, kpr), dtype=torch.uint8, device=a32.device)
     s = torch.empty((R, M, kpr // 32), dtype=torch.uint8, device=a32.device)
     for r in range(R):
-        quantize_mxfp8(a32[:, r * kpr:(r + 1) * kpr], q[r], s[r], stream=stream)
+        quantize_mxfp8(a32[:, r * kpr:(r + 1) * kpr], q[r], s[r], stream=stream, fmt=fmt)
     return q, s

@@ -15,7 +15,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmxgemm_seg.so")
 
-SOURCES = ["kernels.hip", "mxgemm_seg.cpp"]
+# One GEMM translation unit per (A, B) FP8 format pair, compiled in parallel.
+SOURCES = ["kernels.hip", "gemm_e4m3_e4m3.hip", "gemm_e5m2_e5m2.hip", "gemm_e4m3_e5m2.hip",
+           "gemm_e5m2_e4m3.hip", "mxgemm_seg.cpp"]
 ARCH = "gfx950"
 
 # Packed-FP32 ALU forms are switched off for every kernel (the compiler would
@@ -37,17 +39,29 @@ def build(verbose: bool = False) -> str:
     objs = []
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    procs = []
     for src in SOURCES:
         obj = os.path.join(tmpdir, src + ".o")
         cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        if r.returncode != 0:
-            sys.stderr.write(r.stdout + r.stderr)
-            raise RuntimeError(f"hipcc failed on {src}")
+        while sum(p.poll() is None for _, p in procs) >= jobs:
+            procs[[p.poll() is None for _, p in procs].index(True)][1].wait()
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                            text=True)))
         objs.append(obj)
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(src)
+        elif verbose and out:
+            sys.stderr.write(out)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,6 @@
+// GEMM kernels for A E4M3, B E4M3.
+#include "gemm_impl.h"
+
+namespace mxg {
+template hipError_t launch_gemm_fmt<kE4M3, kE4M3>(int, bool, const GemmArgs&, hipStream_t);
+}  // namespace mxg

@@ -63,11 +63,13 @@ struct QuantArgs {
     uint8_t* q;
     uint8_t* s;
     int64_t rows, cols, ld_x, ld_q, ld_s;
+    int fmt;                  // 0 = E4M3, 1 = E5M2
 };
 
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
-// One work-group per work item (a.total_work of them).
-hipError_t launch_gemm(int cfg, bool exact, const GemmArgs& a, hipStream_t stream);
+// One work-group per work item (a.total_work of them); fa, fb: the FP8
+// formats of A and B (0 = E4M3, 1 = E5M2).
+hipError_t launch_gemm(int cfg, bool exact, int fa, int fb, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
 

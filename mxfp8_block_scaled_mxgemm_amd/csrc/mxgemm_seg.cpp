@@ -132,6 +132,15 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
         p->precision = opts->precision;
     }
     const bool exact = p->precision == MXGEMM_PRECISION_EXACT;
+    p->a_format = MXGEMM_FMT_E4M3;
+    p->b_format = MXGEMM_FMT_E4M3;
+    if (opts && opts->a_format >= 0)
+        p->a_format = opts->a_format;
+    if (opts && opts->b_format >= 0)
+        p->b_format = opts->b_format;
+    if ((p->a_format != MXGEMM_FMT_E4M3 && p->a_format != MXGEMM_FMT_E5M2) ||
+        (p->b_format != MXGEMM_FMT_E4M3 && p->b_format != MXGEMM_FMT_E5M2))
+        return fail(MXGEMM_EINVAL, "unknown FP8 format (a %d, b %d)", p->a_format, p->b_format);
 
     // Window size W (chunks per stage/GEMM launch pair).  W = nbuf / 2
     // lets the staging of window w + 1 overlap the GEMM of window w; W =
@@ -486,7 +495,8 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         ga.c_vec4 = ((uintptr_t)ga.c % 8 == 0) && (P.N % 4 == 0);
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[2 * w], st));
-        HIP_TRY(mxg::launch_gemm(P.tile_cfg, P.precision == MXGEMM_PRECISION_EXACT, ga, st));
+        HIP_TRY(mxg::launch_gemm(P.tile_cfg, P.precision == MXGEMM_PRECISION_EXACT, P.a_format,
+                                 P.b_format, ga, st));
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
         if (P.split > 1) {
@@ -567,6 +577,14 @@ int mxgemm_seg_kernel_times(mxgemm_seg_t h, double* gemm_ms, int32_t* gemm_launc
 int mxgemm_quantize_mxfp8(const float* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
                           int64_t ld_q, uint8_t* s, int64_t ld_s, void* stream)
 {
+    return mxgemm_quantize_mx(x, rows, cols, ld_x, q, ld_q, s, ld_s, MXGEMM_FMT_E4M3, stream);
+}
+
+int mxgemm_quantize_mx(const float* x, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* q,
+                       int64_t ld_q, uint8_t* s, int64_t ld_s, int32_t format, void* stream)
+{
+    if (format != MXGEMM_FMT_E4M3 && format != MXGEMM_FMT_E5M2)
+        return fail(MXGEMM_EINVAL, "unknown FP8 format %d", format);
     if (!x || !q || !s)
         return fail(MXGEMM_EINVAL, "NULL pointer");
     if (rows < 0 || cols < 0 || cols % 32 != 0)
@@ -585,6 +603,7 @@ int mxgemm_quantize_mxfp8(const float* x, int64_t rows, int64_t cols, int64_t ld
     a.ld_x = ld_x;
     a.ld_q = ld_q;
     a.ld_s = ld_s;
+    a.fmt = format;
     HIP_TRY(mxg::launch_quantize(a, (hipStream_t)stream));
     return MXGEMM_OK;
 }

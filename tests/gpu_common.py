@@ -46,21 +46,23 @@ def summary(got, ref):
 
 class Case:
     """One workload: fp32 operands, the GPU-quantised device tensors and the
-    oracle-quantised host arrays."""
+    oracle-quantised host arrays; A codes of format fmt_a, B codes of fmt_b
+    (oracle.E4M3 / oracle.E5M2, the same codes as the library's)."""
 
-    def __init__(self, w, a32, b32):
+    def __init__(self, w, a32, b32, fmt_a=oracle.E4M3, fmt_b=oracle.E4M3):
         import torch
         import mxfp8_block_scaled_mxgemm_amd as pkg
         self.w = w
+        self.fmt_a, self.fmt_b = fmt_a, fmt_b
         dev = torch.device("cuda:0")
         self.a32, self.b32 = a32, b32
         a_d = torch.from_numpy(a32).to(dev)
         b_d = torch.from_numpy(b32).to(dev)
-        self.a_q, self.a_s = pkg.quantize_segments(a_d, w.R)
-        self.b_q, self.b_s = pkg.quantize_mxfp8(b_d)
+        self.a_q, self.a_s = pkg.quantize_segments(a_d, w.R, fmt=fmt_a)
+        self.b_q, self.b_s = pkg.quantize_mxfp8(b_d, fmt=fmt_b)
         del a_d, b_d
-        qa, sa = oracle.quantize_mxfp8(a32)
-        self.qb, self.sb = oracle.quantize_mxfp8(b32)
+        qa, sa = oracle.quantize_mxfp8(a32, fmt=fmt_a)
+        self.qb, self.sb = oracle.quantize_mxfp8(b32, fmt=fmt_b)
         self.a_seg = inputs.split_segments(qa, w.R)
         self.s_seg = inputs.split_segments(sa, w.R)
         torch.cuda.synchronize()
@@ -77,6 +79,9 @@ class Case:
         w = self.w
         if c is None:
             c = torch.full((w.M, w.N), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+        if opts is None:
+            opts = pkg.options()
+        opts.a_format, opts.b_format = self.fmt_a, self.fmt_b
         with pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts) as g:
             g.run(self.a_q, self.a_s, self.b_q, self.b_s, c)
             torch.cuda.synchronize()
@@ -84,24 +89,25 @@ class Case:
 
     def oracle_full(self):
         return oracle.bf16_bits_to_float(
-            oracle.mxgemm_seg(self.a_seg, self.s_seg, self.qb, self.sb)).astype(np.float64)
+            oracle.mxgemm_seg(self.a_seg, self.s_seg, self.qb, self.sb, fmt_a=self.fmt_a,
+                              fmt_b=self.fmt_b)).astype(np.float64)
 
     def oracle_entries(self, ms, ns):
         return oracle.bf16_bits_to_float(
-            oracle.mxgemm_seg_entries(self.a_seg, self.s_seg, self.qb, self.sb, ms, ns)
-        ).astype(np.float64)
+            oracle.mxgemm_seg_entries(self.a_seg, self.s_seg, self.qb, self.sb, ms, ns,
+                                      fmt_a=self.fmt_a, fmt_b=self.fmt_b)).astype(np.float64)
 
 
-def workload_case(name):
+def workload_case(name, fmt_a=oracle.E4M3, fmt_b=oracle.E4M3):
     w = inputs.WORKLOADS[name]
     a32, b32 = inputs.fp32_operands(w)
-    return Case(w, a32, b32)
+    return Case(w, a32, b32, fmt_a, fmt_b)
 
 
-def custom_case(R, M, kpr, N, cms, nbuf, seed, sigma=1.0):
+def custom_case(R, M, kpr, N, cms, nbuf, seed, sigma=1.0, fmt_a=oracle.E4M3, fmt_b=oracle.E4M3):
     w = inputs.Workload("custom", R, M, kpr, N, cms, nbuf, sigma, 0.0, 1.0, seed)
     a32, b32 = inputs.fp32_operands(w)
-    return Case(w, a32, b32)
+    return Case(w, a32, b32, fmt_a, fmt_b)
 
 
 def sample_entries(M, N, tile_m, tile_n, seed, count=4096):

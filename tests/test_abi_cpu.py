@@ -62,6 +62,18 @@ def test_plan_options_rules():
     assert (p.tile_cfg, p.split, p.chunks_per_window, p.windows) == (2, 2, 2, 1)
 
 
+def test_plan_formats():
+    p = pkg.plan(128, 256, 2, 256, 64, 2)
+    assert (p.a_format, p.b_format) == (pkg.FMT_E4M3, pkg.FMT_E4M3)
+    p = pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(a_format="e5m2"))
+    assert (p.a_format, p.b_format) == (pkg.FMT_E5M2, pkg.FMT_E4M3)
+    p = pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(a_format=0, b_format=1))
+    assert (p.a_format, p.b_format) == (pkg.FMT_E4M3, pkg.FMT_E5M2)
+    for bad in (dict(a_format=2), dict(b_format=7)):
+        with pytest.raises(pkg.MxgemmError):
+            pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(**bad))
+
+
 def _check_bijection(p, rows):
     tiles_m = -(-rows // p.tile_m)
     total = tiles_m * p.tiles_n * p.split

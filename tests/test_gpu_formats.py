@@ -1,0 +1,181 @@
+"""GPU parity for the E5M2 operand formats: the E5M2 quantiser bit for bit,
+and the GEMM for every (A, B) format pair other than E4M3 x E4M3 against the
+oracle, in both precision modes, on the workloads, on every tile
+configuration of a ragged shape, and on integer data that must come out
+exact."""
+import numpy as np
+import pytest
+
+import oracle
+from mxfp8_block_scaled_mxgemm_amd import inputs
+from gpu_common import (Case, custom_case, sample_entries, say, summary, torch_cuda,
+                        within_tol, workload_case)
+
+pytestmark = pytest.mark.gpu
+
+E4, E5 = oracle.E4M3, oracle.E5M2
+PAIRS = [(E5, E5), (E4, E5), (E5, E4)]
+PAIR_IDS = ["e5m2xe5m2", "e4m3xe5m2", "e5m2xe4m3"]
+
+_CACHE = {}
+
+
+def _case(name, fa, fb):
+    key = (name, fa, fb)
+    if key not in _CACHE:
+        _CACHE.clear()
+        say(f"[case] building inputs for {name} fmt_a={fa} fmt_b={fb}")
+        _CACHE[key] = workload_case(name, fa, fb)
+    return _CACHE[key]
+
+
+def _opts(precision):
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    return pkg.options(precision=pkg.PRECISION_EXACT if precision == "exact"
+                       else pkg.PRECISION_NATIVE)
+
+
+# ------------------------------------------------------------- quantiser --
+
+@pytest.mark.parametrize("name", ["tiny_m128_n256_k512", "m1024_n2048_k4096",
+                                  "skinny_m64_n2048_k7168", "m4096_n4096_k7168"])
+def test_gpu_quantizer_e5m2_bit_exact(name):
+    torch_cuda()
+    case = _case(name, E5, E5)
+    say(f"[quant-e5m2] {name} {case.w.describe()}")
+    assert case.quantizer_matches()
+
+
+def test_gpu_quantizer_e5m2_edge_values():
+    torch = torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((64, 256)).astype(np.float32)
+    x[rng.random(x.shape) < 0.02] *= 1000.0
+    x[3, :32] = 0.0
+    x[4, 32:64] = -0.0
+    x[5, 64:96] = 57344.0
+    x[6, 96:128] = np.float32(57344.0) * np.float32(2.0 ** -30)
+    x[7, 128:160] = np.float32(1e-39)
+    x[8, 160:192] = np.float32(3.0e38)
+    x[9, 192:224] = np.linspace(-1, 1, 32, dtype=np.float32) * np.float32(2.0 ** -130)
+    # amax 57344 -> e = 0: midpoints of the E5M2 grid in the normal range
+    # (ties to even) and in the subnormal range (step 2^-16)
+    x[10, :32] = np.array([57344.0, 1.125, 1.375, 3.0 * 2 ** -17, 2 ** -17, 5 * 2 ** -17,
+                           -1.125, 0.0, 2.5, 3.5, -2.5, 49152.0, 53248.0, -53248.0,
+                           7 * 2 ** -17, 2 ** -14 + 2 ** -17, 0.0] + [0.5] * 15,
+                          dtype=np.float32)[:32]
+    bits = (np.arange(64 * 4 * 32, dtype=np.uint32) * np.uint32(0x00100000 + 0x8000)) & np.uint32(0x47FFFFFF)
+    x[11:15] = bits.view(np.float32).reshape(-1, 256)[:4]
+    q, s = pkg.quantize_mxfp8(torch.from_numpy(x).cuda(), fmt=pkg.FMT_E5M2)
+    qr, sr = oracle.quantize_mxfp8(x, fmt=E5)
+    assert np.array_equal(s.cpu().numpy(), sr)
+    assert np.array_equal(q.cpu().numpy(), qr)
+
+
+# ---------------------------------------------------------------- parity --
+
+@pytest.mark.parametrize("precision", ["exact", "native"])
+@pytest.mark.parametrize("name", ["tiny_m128_n256_k512", "m1024_n2048_k4096",
+                                  "skinny_m64_n2048_k7168"])
+@pytest.mark.parametrize("fa,fb", PAIRS, ids=PAIR_IDS)
+def test_parity_full_formats(fa, fb, name, precision):
+    torch_cuda()
+    case = _case(name, fa, fb)
+    say(f"[parity-fmt] {name} fa={fa} fb={fb} {precision}")
+    got = case.run_gpu(opts=_opts(precision)).float().cpu().numpy()
+    ref = case.oracle_full()
+    say("  " + summary(got, ref))
+    bad, _ = within_tol(got, ref)
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("fa,fb", PAIRS, ids=PAIR_IDS)
+def test_parity_sampled_outlier_formats(fa, fb):
+    """The 8192 x 8192 x 8192 outlier workload in exact mode, sampled."""
+    torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    name = "outlier_m8192_n8192_k8192"
+    case = _case(name, fa, fb)
+    say(f"[parity-fmt-sampled] {name} fa={fa} fb={fb}")
+    got_all = case.run_gpu(opts=_opts("exact")).float().cpu().numpy()
+    assert not np.isnan(got_all).any()
+    w = case.w
+    p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
+    ms, ns = sample_entries(w.M, w.N, p.tile_m, p.tile_n, seed=w.seed + fa + 2 * fb, count=2048)
+    ref = case.oracle_entries(ms, ns)
+    got = got_all[ms, ns]
+    say("  " + summary(got, ref))
+    bad, _ = within_tol(got, ref)
+    assert not bad.any()
+
+
+ONE_SHOT_CFG, ONE_SHOT_STEPS = 6, 8
+
+
+@pytest.mark.parametrize("precision", ["exact", "native"])
+@pytest.mark.parametrize("split", [1, 3])
+@pytest.mark.parametrize("cfg", range(7))
+@pytest.mark.parametrize("fa,fb", PAIRS, ids=PAIR_IDS)
+def test_parity_forced_tiles_formats(fa, fb, cfg, split, precision):
+    """Every tile configuration, split 1 and 3, on the ragged shape (24 rows
+    per chunk, N = 200)."""
+    torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    key = ("ragged", fa, fb)
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = custom_case(R=6, M=120, kpr=256, N=200, cms=24, nbuf=4, seed=9,
+                                  fmt_a=fa, fmt_b=fb)
+        _CACHE[key + ("ref",)] = _CACHE[key].oracle_full()
+    case, ref = _CACHE[key], _CACHE[key + ("ref",)]
+    say(f"[parity-fmt-forced] fa={fa} fb={fb} cfg={cfg} split={split} {precision}")
+    opts = _opts(precision)
+    opts.tile_cfg, opts.split = cfg, split
+    if cfg == ONE_SHOT_CFG and (6 // split) * (256 // 128) > ONE_SHOT_STEPS:
+        with pytest.raises(pkg.MxgemmError):
+            case.run_gpu(opts=opts)
+        return
+    got = case.run_gpu(opts=opts).float().cpu().numpy()
+    bad, _ = within_tol(got, ref)
+    assert not bad.any(), summary(got, ref)
+
+
+@pytest.mark.parametrize("precision", ["exact", "native"])
+@pytest.mark.parametrize("fa,fb", PAIRS, ids=PAIR_IDS)
+def test_integer_data_bit_exact_formats(fa, fb, precision):
+    """Sparse +-1 data: both formats hold +-1 exactly, so C is the integer
+    product, bit for bit."""
+    torch_cuda()
+    R, M, kpr, N, cms, nbuf, dens = 4, 256, 1024, 512, 64, 2, 0.06
+    w = inputs.Workload("sign", R, M, kpr, N, cms, nbuf, 1.0, 0.0, 1.0, 0)
+    xa = inputs.sparse_sign_matrix((M, R * kpr), dens, 91)
+    xb = inputs.sparse_sign_matrix((N, R * kpr), dens, 92)
+    case = Case(w, xa, xb, fa, fb)
+    ref = xa.astype(np.float64) @ xb.astype(np.float64).T
+    assert np.abs(ref).max() <= 256
+    got = case.run_gpu(opts=_opts(precision)).float().cpu().numpy()
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
+def test_format_codes_are_read_as_declared():
+    """The same bytes read under different declared formats give different
+    products: E4M3 x E4M3 codes declared as E5M2 must not match the E4M3
+    oracle (guards against a plan ignoring its format fields)."""
+    torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    import torch
+    case = custom_case(R=2, M=64, kpr=256, N=128, cms=32, nbuf=2, seed=93)
+    # E4M3 codes 0x7C..0x7E are E5M2 infinities / NaNs: move them down
+    qb = case.qb.copy()
+    qb[(qb & 0x7F) >= 0x7C] -= 8
+    case.qb = qb
+    case.b_q = torch.from_numpy(qb).cuda()
+    ref = case.oracle_full()
+    case.fmt_b = E5                     # declare the E4M3 B codes as E5M2
+    got = case.run_gpu().float().cpu().numpy()
+    bad, _ = within_tol(got, ref)
+    assert bad.mean() > 0.5
+    ref_e5 = case.oracle_full()         # the oracle reading B as E5M2 agrees
+    bad, _ = within_tol(got, ref_e5)
+    assert not bad.any()
