@@ -75,7 +75,7 @@ enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
 typedef struct mxgemm_seg_plan {
     int64_t M, kPerRank, N, K, commMSize;
     int32_t rank_size, buffer_count;
-    int32_t chunks;            /* M / commMSize                             */
+    int32_t chunks;            /* ceil(M / commMSize)                       */
     int32_t chunks_per_window; /* W: chunks one stage/GEMM launch pair covers */
     int32_t windows;           /* ceil(chunks / W)                          */
     int32_t window_slots;      /* buffer_count / W ring windows             */
@@ -113,12 +113,14 @@ typedef struct mxgemm_seg_options {
  *   kPerRank   K columns per rank segment              (> 0, % 128 == 0)
  *   rank_size  R, number of (simulated) ranks          (1 .. 64)
  *   N          columns of C, rows of B ([N][K])        (> 0)
- *   commMSize  rows per staged chunk                   (> 0, divides M)
+ *   commMSize  rows per staged chunk                   (> 0)
  *   buffer_count  staging ring depth                   (power of two, 1..64)
  * Rules follow all_to_all_matmul.cpp (argument parsing: positive sizes, K
  * divisible by rankNum) and all_to_all_matmul_impl.h (MatmulProcess: the
- * ring index is a bit mask, so the depth is a power of two; CalcMOffset /
- * GetCurMSize: chunks have no tail, so commMSize divides M).  The MX block is
+ * ring index is a bit mask, so the depth is a power of two).  There,
+ * CalcMOffset / GetCurMSize size every chunk at commMSize rows, so rows past
+ * the last whole chunk would be dropped; here the last chunk holds the
+ * remaining M % commMSize rows when commMSize does not divide M.  The MX block is
  * 32; this build also needs kPerRank % 128 == 0 (one MFMA K-step), else
  * MXGEMM_EUNSUPPORTED.  Allocates, on the current device, the staging ring
  * (buffer_count * R * commMSize * kPerRank * 33/32 bytes), the split-K
@@ -138,15 +140,16 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
  * Enqueue one segmented GEMM on `stream`; returns once enqueued (no host
  * synchronisation).  All pointers are device memory, 16-byte aligned, owned
  * by the caller, and must stay valid until the work completes:
- *   a_seg    uint8 E4M3  [R][M][kPerRank]     segment r is rank r's K range
+ *   a_seg    uint8 FP8   [R][M][kPerRank]     segment r is rank r's K range
  *   a_scale  uint8 E8M0  [R][M][kPerRank/32]
- *   b        uint8 E4M3  [N][K], K = R*kPerRank, K contiguous (B transposed)
+ *   b        uint8 FP8   [N][K], K = R*kPerRank, K contiguous (B transposed)
+ * (FP8 codes in the plan's a_format / b_format, E4M3 by default)
  *   b_scale  uint8 E8M0  [N][K/32]
  *   c        bfloat16    [M][N], fully overwritten
  * Layouts: all_to_all_comm_udma.h, PutSegmentToRank / PutScaleToRank (source
  * offsets r*M*rowBytes + mOffset*rowBytes), all_to_all_matmul.cpp (host
  * buffer sizes), all_to_all_matmul_impl.h (TransB = true, C offset
- * mOffset * N).  Chunk j (rows [j*commMSize, (j+1)*commMSize) of every
+ * mOffset * N).  Chunk j (rows [j*commMSize, min((j+1)*commMSize, M)) of every
  * segment, with their scales) is copied by a staging kernel on the handle's
  * side stream into ring slot j % buffer_count; the GEMM for a chunk starts
  * only after its copy (ready event) and a slot is refilled only after the

@@ -49,8 +49,11 @@ __global__ void __launch_bounds__(256) stage_kernel(StageArgs p)
     const int r = pair - cidx * p.R;
     const int64_t j = p.chunk0 + cidx;
     const int64_t slot = j & (p.nbuf - 1);
+    // rows of chunk j: commMSize, or what is left of M for the last chunk
+    const int64_t left = p.M - j * p.cms;
+    const int64_t nrows = left < p.cms ? left : p.cms;
     if (!is_scale) {
-        const int64_t len16 = (p.cms * p.kpr) >> 4;
+        const int64_t len16 = (nrows * p.kpr) >> 4;
         const u32x4* src = reinterpret_cast<const u32x4*>(p.a_seg + (r * p.M + j * p.cms) * p.kpr);
         u32x4* dst = reinterpret_cast<u32x4*>(p.ring + slot * p.slot_bytes + r * p.cms * p.kpr);
         const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -58,7 +61,7 @@ __global__ void __launch_bounds__(256) stage_kernel(StageArgs p)
             dst[i] = __builtin_nontemporal_load(src + i);
     } else {
         const int64_t sk = p.kpr >> 5;
-        const int64_t len4 = (p.cms * sk) >> 2;
+        const int64_t len4 = (nrows * sk) >> 2;
         const uint32_t* src =
             reinterpret_cast<const uint32_t*>(p.sa_seg + (r * p.M + j * p.cms) * sk);
         uint32_t* dst =

@@ -52,9 +52,6 @@ int validate(int64_t M, int64_t kpr, int32_t R, int64_t N, int64_t cms, int32_t 
         return fail(MXGEMM_EINVAL, "rank_size %d exceeds 64", R);
     if (!is_pow2(nbuf) || nbuf > 64)
         return fail(MXGEMM_EINVAL, "buffer_count %d must be a power of two in [1, 64]", nbuf);
-    if (M % cms != 0)
-        return fail(MXGEMM_EINVAL, "commMSize %lld must divide M %lld (chunks have no tail)",
-                    (long long)cms, (long long)M);
     if (kpr % 32 != 0)
         return fail(MXGEMM_EINVAL, "kPerRank %lld must be a multiple of the MX block 32",
                     (long long)kpr);
@@ -67,7 +64,7 @@ int validate(int64_t M, int64_t kpr, int32_t R, int64_t N, int64_t cms, int32_t 
     const int64_t ring = (int64_t)nbuf * R * cms * kpr;
     if (ring >= (1LL << 31))
         return fail(MXGEMM_EUNSUPPORTED, "staging ring of %lld bytes exceeds 2 GiB", (long long)ring);
-    if ((M / cms) > (1 << 30))
+    if (ceil_div(M, cms) > (1 << 30))
         return fail(MXGEMM_EUNSUPPORTED, "too many chunks");
     return MXGEMM_OK;
 }
@@ -123,7 +120,7 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     p->commMSize = cms;
     p->rank_size = R;
     p->buffer_count = nbuf;
-    p->chunks = (int32_t)(M / cms);
+    p->chunks = (int32_t)ceil_div(M, cms);   // the last chunk may be short
     p->num_cus = num_cus;
     p->precision = MXGEMM_PRECISION_EXACT;
     if (opts && opts->precision >= 0) {
@@ -471,7 +468,11 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
 
         // consumer: GEMM over the window once its chunks have landed
         HIP_TRY(hipStreamWaitEvent(st, h->ready[g], 0));
-        const int64_t rows = (int64_t)nch * P.commMSize;
+        // rows of the window: whole chunks, except that the last chunk of
+        // the problem holds only the rows left
+        const int64_t rows_left = P.M - (int64_t)chunk0 * P.commMSize;
+        const int64_t rows = (int64_t)nch * P.commMSize < rows_left ? (int64_t)nch * P.commMSize
+                                                                       : rows_left;
         mxg::GemmArgs ga;
         ga.a = h->ring + (int64_t)g * P.chunks_per_window * P.slot_bytes;
         ga.as = h->sring + (int64_t)g * P.chunks_per_window * P.scale_slot_bytes;

@@ -38,7 +38,6 @@ def test_version_and_empty_error():
     ((0, 256, 2, 256, 64, 2), pkg._lib.MXGEMM_EINVAL),        # empty M
     ((128, 256, 2, 0, 64, 2), pkg._lib.MXGEMM_EINVAL),        # empty N
     ((128, 256, 0, 256, 64, 2), pkg._lib.MXGEMM_EINVAL),      # no ranks
-    ((128, 256, 2, 256, 48, 2), pkg._lib.MXGEMM_EINVAL),      # commMSize does not divide M
     ((128, 256, 2, 256, 64, 3), pkg._lib.MXGEMM_EINVAL),      # ring depth not a power of 2
     ((128, 48, 2, 256, 64, 2), pkg._lib.MXGEMM_EINVAL),       # not a multiple of the MX block
     ((128, 96, 2, 256, 64, 2), pkg._lib.MXGEMM_EUNSUPPORTED), # MX-aligned, not MFMA-aligned
@@ -60,6 +59,14 @@ def test_plan_options_rules():
         pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(tile_cfg=99))
     p = pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(tile_cfg=2, split=2, chunks_per_window=2))
     assert (p.tile_cfg, p.split, p.chunks_per_window, p.windows) == (2, 2, 2, 1)
+
+
+def test_plan_chunk_tail():
+    """commMSize need not divide M: the last chunk holds the rows left."""
+    p = pkg.plan(130, 256, 2, 256, 48, 2)
+    assert p.chunks == 3 and p.windows * p.chunks_per_window >= 3
+    p = pkg.plan(1, 256, 2, 256, 64, 4)
+    assert p.chunks == 1
 
 
 def test_plan_formats():

@@ -212,6 +212,44 @@ def test_parity_forced_tiles_ragged(cfg, split, precision):
     assert not bad.any(), summary(got, ref)
 
 
+@pytest.mark.parametrize("precision", ["exact", "native"])
+@pytest.mark.parametrize("shape", [
+    (4, 130, 256, 200, 48, 2),      # last chunk 34 of 48 rows
+    (2, 1, 128, 64, 64, 4),         # one row: a single short chunk
+    (8, 70, 896, 2048, 8, 4),       # skinny geometry with a 6-row last chunk
+    (3, 1000, 384, 520, 96, 4),     # 11 chunks, last 40 rows, odd R
+])
+def test_parity_chunk_tail(shape, precision):
+    """commMSize not dividing M: the last chunk carries the rows left, and
+    every row of C is computed (none dropped)."""
+    torch_cuda()
+    R, M, kpr, N, cms, nbuf = shape
+    say(f"[parity-tail] R={R} M={M} kpr={kpr} N={N} cms={cms} nbuf={nbuf} {precision}")
+    case = custom_case(R=R, M=M, kpr=kpr, N=N, cms=cms, nbuf=nbuf, seed=17 + M)
+    got = case.run_gpu(opts=_opts(precision)).float().cpu().numpy()
+    ref = case.oracle_full()
+    say("  " + summary(got, ref))
+    bad, _ = within_tol(got, ref)
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("cfg", range(7))
+def test_parity_chunk_tail_forced_tiles(cfg):
+    """Every tile configuration on a shape whose last chunk is short."""
+    torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    key = "tail"
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = custom_case(R=4, M=90, kpr=256, N=136, cms=40, nbuf=2, seed=23)
+        _CACHE[key + "ref"] = _CACHE[key].oracle_full()
+    case, ref = _CACHE[key], _CACHE[key + "ref"]
+    say(f"[parity-tail-forced] cfg={cfg}")
+    got = case.run_gpu(opts=pkg.options(tile_cfg=cfg)).float().cpu().numpy()
+    bad, _ = within_tol(got, ref)
+    assert not bad.any(), summary(got, ref)
+
+
 @pytest.mark.parametrize("W", [1, 2, 4])
 def test_parity_window_sizes(W):
     torch_cuda()
