@@ -159,6 +159,8 @@ def main():
     ap.add_argument("--tile-cfg", type=int, default=-1)
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--window", type=int, default=-1)
+    ap.add_argument("--ring", choices=["auto", "events", "flags"], default="auto",
+                    help="ring protocol (default: the planner's choice)")
     ap.add_argument("--precision", choices=["exact", "native"], default="exact",
                     help="GEMM arithmetic (default exact: parity-green on every workload)")
     ap.add_argument("--a-format", choices=["e4m3", "e5m2"], default="e4m3",
@@ -216,9 +218,10 @@ def main():
     prec = pkg.PRECISION_EXACT if args.precision == "exact" else pkg.PRECISION_NATIVE
     fmts = (args.a_format, args.b_format)
     if (args.tile_cfg >= 0 or args.split > 0 or args.window > 0 or prec != pkg.PRECISION_EXACT
-            or fmts != ("e4m3", "e4m3")):
+            or fmts != ("e4m3", "e4m3") or args.ring != "auto"):
         opts = pkg.options(tile_cfg=args.tile_cfg, split=args.split, chunks_per_window=args.window,
-                           precision=prec, a_format=args.a_format, b_format=args.b_format)
+                           precision=prec, a_format=args.a_format, b_format=args.b_format,
+                           ring=-1 if args.ring == "auto" else args.ring)
     g = pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts)
     plan = g.plan.as_dict()
     log(f"[bench] plan: {plan}")
@@ -322,12 +325,15 @@ def main():
     g.set_profiling(False)
     torch.cuda.synchronize()
     gemm_ms_per_launch = kt["gemm_ms"] / kt["gemm_launches"]
-    stage_ms_per_launch = kt["stage_ms"] / kt["stage_launches"]
+    stage_ms_per_launch = kt["stage_ms"] / max(1, kt["stage_launches"])
     flops = float(w.flops)
-    flops_per_launch = flops / plan["windows"]
-    # algorithmic bytes of one GEMM launch (a window of M / windows rows on
-    # average): A rows and B with their E8M0 scales, C in bfloat16
-    rows_w = w.M / plan["windows"]
+    # GEMM launches per step: one per window (events protocol), or one
+    # persistent launch that also stages (flags protocol)
+    launches = 1 if plan["ring"] == pkg.RING_FLAGS else plan["windows"]
+    flops_per_launch = flops / launches
+    # algorithmic bytes of one GEMM launch (M / launches rows on average):
+    # A rows and B with their E8M0 scales, C in bfloat16
+    rows_w = w.M / launches
     bytes_per_launch = (rows_w * w.K + w.N * w.K) * 33 / 32 + rows_w * w.N * 2
     kernel_peak = PEAK_BF16_TFLOPS if args.precision == "exact" else PEAK_FP8_TFLOPS
     # the roofline that bounds the launch: HBM when its arithmetic intensity
@@ -339,7 +345,7 @@ def main():
     else:
         achieved = flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
         roof_peak, roof_unit = kernel_peak, "TFLOP/s"
-    log(f"[bench] kernels: gemm {gemm_ms_per_launch * 1e3:.2f} us/launch x{plan['windows']}, "
+    log(f"[bench] kernels: gemm {gemm_ms_per_launch * 1e3:.2f} us/launch x{launches}, "
         f"stage {stage_ms_per_launch * 1e3:.2f} us/launch")
 
     if sampler is not None:
@@ -377,7 +383,7 @@ def main():
                    "flop_per_step": w.flops,
                    "algorithmic_bytes_per_step": w.algorithmic_bytes,
                    "plan": {k: plan[k] for k in ("tile_m", "tile_n", "split", "chunks_per_window",
-                                                 "windows", "grid")}},
+                                                 "windows", "grid", "ring")}},
         "pct_of_mxfp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "hbm_frac_end_to_end": round(w.algorithmic_bytes / (ms_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "timer": (("replays of one HIP-graph-captured step" if timer == "graph" else "stream-issued steps")
@@ -408,7 +414,7 @@ def main():
             "bytes_per_launch": int(bytes_per_launch),
             "traffic": traffic,
             "gemm_us_per_launch": round(gemm_ms_per_launch * 1e3, 3),
-            "launches_per_step": plan["windows"],
+            "launches_per_step": launches,
             "stage_us_per_launch": round(stage_ms_per_launch * 1e3, 3),
         },
         "kernel_source_sha": sha,

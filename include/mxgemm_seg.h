@@ -40,8 +40,9 @@ enum {
     MXGEMM_EINVAL = -1,        /* an argument breaks a documented rule      */
     MXGEMM_ENOMEM = -2,        /* device allocation failed                  */
     MXGEMM_EHIP = -3,          /* a HIP runtime call failed                 */
-    MXGEMM_EUNSUPPORTED = -4   /* valid, but not supported by this build or
+    MXGEMM_EUNSUPPORTED = -4,  /* valid, but not supported by this build or
                                   device (not gfx950, shape limits)         */
+    MXGEMM_ETIMEOUT = -5       /* flags protocol: a device wait gave up     */
 };
 
 typedef struct mxgemm_seg* mxgemm_seg_t;
@@ -70,6 +71,29 @@ enum { MXGEMM_PRECISION_EXACT = 0, MXGEMM_PRECISION_NATIVE = 1 };
  * native mode passes the formats to the scaled MFMA. */
 enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
 
+/* Ring protocols: how a GEMM learns that a chunk has landed in the ring
+ * and the staging side that a slot may be refilled.  Both are on the
+ * pages (all_to_all_matmul_impl.h, MatmulProcess / AllToAllProcess).
+ *
+ *  MXGEMM_RING_EVENTS: per window of W chunks, a staging kernel on the
+ *    handle's side stream, a ready event, the GEMM launch (and a split-K
+ *    sum) on the caller's stream, a credit event.
+ *
+ *  MXGEMM_RING_FLAGS: one persistent launch per run.  Work-group b keeps
+ *    tile column b / S of C (64 columns) and K-split b % S for the whole
+ *    run, holds its B tile (64 rows x the split's K range, at most 1024) in
+ *    LDS, stages its share of every window into the ring, and hands over
+ *    through counters in device memory: ready and credit per (slot group,
+ *    split), polled with agent-scope acquire and released with agent-scope
+ *    release.  The last split to finish a tile sums the FP32 partials in
+ *    split order.  One launch and one read of B instead of one per window:
+ *    for short M (skinny shapes).  Exact precision only.  All work-groups
+ *    must be resident at once (at most one per compute unit); a wait that
+ *    polls spin_limit times without progress gives up, marks the handle
+ *    (mxgemm_seg_status) and lets the kernel finish, so a run never hangs.
+ */
+enum { MXGEMM_RING_EVENTS = 0, MXGEMM_RING_FLAGS = 1 };
+
 /* Plan chosen for a problem: filled by mxgemm_seg_plan (host only, no GPU)
  * and by mxgemm_seg_get_plan for a live handle. */
 typedef struct mxgemm_seg_plan {
@@ -91,6 +115,8 @@ typedef struct mxgemm_seg_plan {
     int32_t precision;         /* MXGEMM_PRECISION_*                        */
     int32_t a_format;          /* MXGEMM_FMT_* of the A codes               */
     int32_t b_format;          /* MXGEMM_FMT_* of the B codes               */
+    int32_t ring;              /* MXGEMM_RING_*                             */
+    int32_t spin_limit;        /* flags protocol: polls before a wait gives up */
     int32_t reserved;
     int64_t slot_bytes;        /* one staging buffer: R*commMSize*kPerRank  */
     int64_t scale_slot_bytes;  /* its scales: R*commMSize*kPerRank/32       */
@@ -105,6 +131,8 @@ typedef struct mxgemm_seg_options {
     int32_t precision;         /* MXGEMM_PRECISION_* (-1 = EXACT)           */
     int32_t a_format;          /* MXGEMM_FMT_* of A (-1 = E4M3)             */
     int32_t b_format;          /* MXGEMM_FMT_* of B (-1 = E4M3)             */
+    int32_t ring;              /* MXGEMM_RING_* (-1 = planner's choice)     */
+    int32_t spin_limit;        /* flags protocol: polls per wait (-1 = ~1 s) */
 } mxgemm_seg_options_t;
 
 /*
@@ -165,6 +193,15 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
  */
 int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const void* b,
                    const void* b_scale, void* c, void* stream);
+
+/*
+ * Flags protocol: MXGEMM_ETIMEOUT if a device wait of any run since the
+ * last call gave up (the work-groups of a run were not all resident at
+ * once, e.g. another kernel held compute units; C of such a run is
+ * undefined), else MXGEMM_OK; clears the mark.  Waits for all work on the
+ * device.  Always MXGEMM_OK for the events protocol.
+ */
+int mxgemm_seg_status(mxgemm_seg_t h);
 
 /* Wait for the handle's work and free everything create() allocated.
  * NULL is accepted.  Errors: EHIP (resources are still released). */

@@ -17,14 +17,15 @@ MXGEMM_EINVAL = -1
 MXGEMM_ENOMEM = -2
 MXGEMM_EHIP = -3
 MXGEMM_EUNSUPPORTED = -4
+MXGEMM_ETIMEOUT = -5
 _NAMES = {MXGEMM_EINVAL: "EINVAL", MXGEMM_ENOMEM: "ENOMEM", MXGEMM_EHIP: "EHIP",
-          MXGEMM_EUNSUPPORTED: "EUNSUPPORTED"}
+          MXGEMM_EUNSUPPORTED: "EUNSUPPORTED", MXGEMM_ETIMEOUT: "ETIMEOUT"}
 
 EXPORTED = [
     "mxgemm_seg_create", "mxgemm_seg_create_ex", "mxgemm_seg_run", "mxgemm_seg_destroy",
     "mxgemm_seg_last_error", "mxgemm_seg_get_plan", "mxgemm_seg_plan", "mxgemm_seg_decode",
     "mxgemm_quantize_mxfp8", "mxgemm_quantize_mx", "mxgemm_seg_set_profiling",
-    "mxgemm_seg_kernel_times", "mxgemm_seg_version",
+    "mxgemm_seg_kernel_times", "mxgemm_seg_status", "mxgemm_seg_version",
 ]
 
 
@@ -45,7 +46,8 @@ class Plan(ctypes.Structure):
         ("split", ctypes.c_int32), ("tiles_m", ctypes.c_int32), ("tiles_n", ctypes.c_int32),
         ("work_items", ctypes.c_int32), ("grid", ctypes.c_int32), ("group_n", ctypes.c_int32),
         ("num_cus", ctypes.c_int32), ("precision", ctypes.c_int32),
-        ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32),
+        ("ring", ctypes.c_int32), ("spin_limit", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("slot_bytes", ctypes.c_int64), ("scale_slot_bytes", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
     ]
@@ -58,6 +60,8 @@ PRECISION_EXACT = 0
 PRECISION_NATIVE = 1
 FMT_E4M3 = 0
 FMT_E5M2 = 1
+RING_EVENTS = 0
+RING_FLAGS = 1
 
 
 def _fmt(f) -> int:
@@ -73,12 +77,22 @@ class Options(ctypes.Structure):
     _fields_ = [("tile_cfg", ctypes.c_int32), ("split", ctypes.c_int32),
                 ("chunks_per_window", ctypes.c_int32),
                 ("precision", ctypes.c_int32),
-                ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32)]
+                ("a_format", ctypes.c_int32), ("b_format", ctypes.c_int32),
+                ("ring", ctypes.c_int32), ("spin_limit", ctypes.c_int32)]
+
+
+def _ring(r) -> int:
+    if r is None or r == -1:
+        return -1
+    if isinstance(r, str):
+        return {"events": RING_EVENTS, "flags": RING_FLAGS}[r.lower()]
+    return int(r)
 
 
 def options(tile_cfg=-1, split=-1, chunks_per_window=-1, precision=-1, a_format=-1,
-            b_format=-1) -> Options:
-    return Options(tile_cfg, split, chunks_per_window, precision, _fmt(a_format), _fmt(b_format))
+            b_format=-1, ring=-1, spin_limit=-1) -> Options:
+    return Options(tile_cfg, split, chunks_per_window, precision, _fmt(a_format), _fmt(b_format),
+                   _ring(ring), spin_limit)
 
 
 _lib = None
@@ -109,12 +123,13 @@ def load():
     lib.mxgemm_quantize_mxfp8.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, vp]
     lib.mxgemm_quantize_mx.argtypes = [vp, i64, i64, i64, vp, i64, vp, i64, i32, vp]
     lib.mxgemm_seg_set_profiling.argtypes = [vp, i32]
+    lib.mxgemm_seg_status.argtypes = [vp]
     lib.mxgemm_seg_kernel_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), p32,
                                             ctypes.POINTER(ctypes.c_double), p32]
     for name in ("mxgemm_seg_create", "mxgemm_seg_create_ex", "mxgemm_seg_run",
                  "mxgemm_seg_destroy", "mxgemm_seg_get_plan", "mxgemm_seg_plan",
                  "mxgemm_seg_decode", "mxgemm_quantize_mxfp8", "mxgemm_quantize_mx",
-                 "mxgemm_seg_set_profiling",
+                 "mxgemm_seg_set_profiling", "mxgemm_seg_status",
                  "mxgemm_seg_kernel_times"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -206,6 +221,11 @@ class SegGemm:
         check(load().mxgemm_seg_run(self._h, ctypes.c_void_p(a_seg), ctypes.c_void_p(a_scale),
                                     ctypes.c_void_p(b), ctypes.c_void_p(b_scale),
                                     ctypes.c_void_p(c), ctypes.c_void_p(stream_handle)))
+
+    def status(self):
+        """Raise MxgemmError(ETIMEOUT) if a device wait of the flags
+        protocol gave up since the last call (waits for the device)."""
+        check(load().mxgemm_seg_status(self._h))
 
     def set_profiling(self, enable: bool):
         check(load().mxgemm_seg_set_profiling(self._h, 1 if enable else 0))

@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "libmxgemm_seg.so")
 
 # One GEMM translation unit per (A, B) FP8 format pair, compiled in parallel.
 SOURCES = ["kernels.hip", "gemm_e4m3_e4m3.hip", "gemm_e5m2_e5m2.hip", "gemm_e4m3_e5m2.hip",
-           "gemm_e5m2_e4m3.hip", "mxgemm_seg.cpp"]
+           "gemm_e5m2_e4m3.hip", "ring.hip", "mxgemm_seg.cpp"]
 ARCH = "gfx950"
 
 # Packed-FP32 ALU forms are switched off for every kernel (the compiler would

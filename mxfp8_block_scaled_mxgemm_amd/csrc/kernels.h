@@ -66,6 +66,43 @@ struct QuantArgs {
     int fmt;                  // 0 = E4M3, 1 = E5M2
 };
 
+// Device-flag ring: one persistent launch per run.  Work-group b owns tile
+// column b / split of C and K-split b % split for the whole run; it keeps
+// its B tile (kRingBN rows x the split's K range) in LDS, stages its share
+// of every window's chunks into the ring, and multiplies the window's rows
+// once the other members of its split group have staged theirs.
+constexpr int kRingBM = 32, kRingBN = 64;
+constexpr int kRingMaxSteps = 8;          // K-steps of 128 per split (LDS)
+constexpr int kRingThreads = 256;
+
+struct RingArgs {
+    const uint8_t* a_seg;     // [R][M][kpr]
+    const uint8_t* sa_seg;    // [R][M][kpr/32]
+    uint8_t* ring;            // [nbuf][R][cms][kpr]
+    uint8_t* sring;           // [nbuf][R][cms][kpr/32]
+    const uint8_t* b;         // [N][K]
+    const uint8_t* bs;        // [N][K/32]
+    uint16_t* c;              // [M][N]
+    float* ws;                // split-K partials [split][M][N] (split > 1)
+    uint32_t* sync;           // counters, zero between runs (ring_sync_words)
+    uint32_t* err;            // set nonzero when a wait gives up
+    int64_t M, kpr, cms, slot_bytes, scale_slot_bytes;
+    int R, N, K, nbuf, chunks, W, windows, window_slots;
+    int tiles_n, split, segs_per_split, tiles_m_win;
+    int c_vec4;               // C rows may be written 4 elements at a time
+    int spin_limit;           // polls before a wait gives up
+};
+
+// 32-bit counters a run of the flags protocol uses: ready and credit per
+// (slot group, split), one per (window, tile row, tile column), and `done`.
+__host__ __device__ inline int64_t ring_sync_words(int window_slots, int split, int windows, int tiles_m_win,
+                               int tiles_n)
+{
+    return 2LL * window_slots * split + (int64_t)windows * tiles_m_win * tiles_n + 1;
+}
+
+hipError_t launch_ring(const RingArgs& a, int fa, int fb, hipStream_t stream);
+
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 // One work-group per work item (a.total_work of them); fa, fb: the FP8
 // formats of A and B (0 = E4M3, 1 = E5M2).

@@ -104,6 +104,39 @@ double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int s
     return total;
 }
 
+// Flags protocol: the split (a divisor of R) whose K range fits the
+// kernel's LDS and whose grid fits one work-group per compute unit, the
+// largest such grid; 0 if none.
+int ring_split(int64_t kpr, int32_t R, int64_t N, int num_cus)
+{
+    const int64_t tiles_n = ceil_div(N, mxg::kRingBN);
+    int best = 0;
+    for (int s = 1; s <= R; ++s) {
+        if (R % s != 0 || (int64_t)(R / s) * (kpr / 128) > mxg::kRingMaxSteps)
+            continue;
+        if (tiles_n * s > num_cus)
+            continue;
+        if (best == 0 || tiles_n * s > tiles_n * best)
+            best = s;
+    }
+    return best;
+}
+
+// Estimated time of a flags-protocol run, in 2.4 GHz clocks: launch and
+// first hand-over, one hand-over per further window, the bytes one
+// work-group copies at the per-CU copy rate (~12 B/clock), and the MFMA and
+// conversion work of its tile rows.
+double estimate_ring(int64_t M, int64_t kpr, int32_t R, int s, int windows, int tiles_m_win)
+{
+    const double kr = (double)(R / s) * kpr * 33.0 / 32.0;
+    const double bytes = kr * (mxg::kRingBN + (double)M);
+    const double steps = (double)(R / s) * (kpr / 128);
+    return 12000.0 + 5000.0 * (windows - 1) + bytes / 12.0 +
+           (double)windows * tiles_m_win * steps * 350.0;
+}
+
+constexpr int kDefaultSpinLimit = 1 << 19;
+
 int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N, int64_t cms,
               int32_t nbuf, int32_t num_cus, const mxgemm_seg_options_t* opts)
 {
@@ -226,6 +259,54 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     p->slot_bytes = (int64_t)R * cms * kpr;
     p->scale_slot_bytes = (int64_t)R * cms * (kpr / 32);
     p->workspace_bytes = p->split > 1 ? (int64_t)p->split * rows * N * 4 : 0;
+    p->ring = MXGEMM_RING_EVENTS;
+    p->spin_limit = opts && opts->spin_limit >= 0 ? opts->spin_limit : kDefaultSpinLimit;
+
+    // Flags protocol: when the options allow it and it is estimated faster
+    // (or it is asked for)
+    const int want = opts ? opts->ring : -1;
+    if (want != -1 && want != MXGEMM_RING_EVENTS && want != MXGEMM_RING_FLAGS)
+        return fail(MXGEMM_EINVAL, "unknown ring protocol %d", want);
+    if (want == MXGEMM_RING_EVENTS)
+        return MXGEMM_OK;
+    const bool forced_tiles = opts && (opts->tile_cfg >= 0 || opts->split > 0);
+    int s = exact && !forced_tiles ? ring_split(kpr, R, N, num_cus) : 0;
+    const int Wr = opts && opts->chunks_per_window > 0 ? opts->chunks_per_window
+                                                       : (nbuf > 1 ? nbuf / 2 : 1);
+    const int64_t windows_r = ceil_div(p->chunks, Wr);
+    const int64_t tiles_m_win = ceil_div((int64_t)Wr * cms, mxg::kRingBM);
+    const int64_t tiles_n_r = ceil_div(N, mxg::kRingBN);
+    if (s > 0) {
+        const int64_t words = mxg::ring_sync_words(nbuf / Wr, s, (int)windows_r, (int)tiles_m_win,
+                                                   (int)tiles_n_r);
+        const int64_t ws = s > 1 ? (int64_t)s * M * N * 4 : 0;
+        if (words > (1 << 20) || ws > (1LL << 32))
+            s = 0;
+    }
+    if (s == 0) {
+        if (want == MXGEMM_RING_FLAGS)
+            return fail(MXGEMM_EUNSUPPORTED, "the flags protocol needs exact precision, no forced "
+                        "tile or split, a split whose K range is at most %d K-steps of 128 and at "
+                        "most one work-group per compute unit (%d)", mxg::kRingMaxSteps, num_cus);
+        return MXGEMM_OK;
+    }
+    const double ring_cost = estimate_ring(M, kpr, R, s, (int)windows_r, (int)tiles_m_win);
+    if (want != MXGEMM_RING_FLAGS && ring_cost >= best.cost)
+        return MXGEMM_OK;
+    p->ring = MXGEMM_RING_FLAGS;
+    p->chunks_per_window = Wr;
+    p->windows = (int32_t)windows_r;
+    p->window_slots = nbuf / Wr;
+    p->tile_cfg = -1;
+    p->tile_m = mxg::kRingBM;
+    p->tile_n = mxg::kRingBN;
+    p->split = s;
+    p->tiles_m = (int32_t)tiles_m_win;
+    p->tiles_n = (int32_t)tiles_n_r;
+    p->work_items = (int32_t)(tiles_n_r * s);
+    p->grid = p->work_items;
+    p->group_n = 1;
+    p->workspace_bytes = s > 1 ? (int64_t)s * M * N * 4 : 0;
     return MXGEMM_OK;
 }
 
@@ -237,6 +318,7 @@ struct mxgemm_seg {
     uint8_t* ring;
     uint8_t* sring;
     float* ws;
+    uint32_t* sync;   // flags protocol: counters, then the error word
     hipStream_t side;
     hipEvent_t start;
     std::vector<hipEvent_t> ready, credit;
@@ -272,6 +354,8 @@ void release(mxgemm_seg* h)
         (void)hipFree(h->sring);
     if (h->ws)
         (void)hipFree(h->ws);
+    if (h->sync)
+        (void)hipFree(h->sync);
     delete h;
 }
 
@@ -280,6 +364,14 @@ int harvest(mxgemm_seg* h)
     if (!h->pending)
         return MXGEMM_OK;
     h->pending = false;
+    if (h->plan.ring == MXGEMM_RING_FLAGS) {
+        HIP_TRY(hipEventSynchronize(h->gemm_ev[1]));
+        float ms = 0.f;
+        HIP_TRY(hipEventElapsedTime(&ms, h->gemm_ev[0], h->gemm_ev[1]));
+        h->gemm_ms += ms;
+        h->gemm_n += 1;
+        return MXGEMM_OK;
+    }
     const int nw = h->plan.windows;
     HIP_TRY(hipEventSynchronize(h->gemm_ev[2 * nw - 1]));
     HIP_TRY(hipEventSynchronize(h->stage_ev[2 * nw - 1]));
@@ -322,6 +414,8 @@ int mxgemm_seg_decode(const mxgemm_seg_plan_t* plan, int64_t rows, int32_t w, in
 {
     if (!plan || rows <= 0 || rows > (int64_t)plan->chunks_per_window * plan->commMSize)
         return fail(MXGEMM_EINVAL, "bad plan or rows");
+    if (plan->ring != MXGEMM_RING_EVENTS)
+        return fail(MXGEMM_EINVAL, "work IDs are decoded for the events protocol only");
     const int tiles_m = (int)ceil_div(rows, plan->tile_m);
     const int total = tiles_m * plan->tiles_n * plan->split;
     const int grid = total;   // one work-group per work item
@@ -376,6 +470,18 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
         return oom("staging scale ring", sring_bytes);
     if (plan.workspace_bytes > 0 && hipMalloc((void**)&h->ws, plan.workspace_bytes) != hipSuccess)
         return oom("split-K workspace", plan.workspace_bytes);
+    if (plan.ring == MXGEMM_RING_FLAGS) {
+        // counters start at zero; each run leaves them at zero
+        const size_t bytes = 4 * (size_t)(mxg::ring_sync_words(plan.window_slots, plan.split,
+                                                               plan.windows, plan.tiles_m,
+                                                               plan.tiles_n) + 1);
+        if (hipMalloc((void**)&h->sync, bytes) != hipSuccess)
+            return oom("ring counters", bytes);
+        if (hipMemset(h->sync, 0, bytes) != hipSuccess) {
+            release(h);
+            return fail(MXGEMM_EHIP, "clearing the ring counters failed");
+        }
+    }
     hipError_t e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
     if (e == hipSuccess)
         e = hipEventCreateWithFlags(&h->start, hipEventDisableTiming);
@@ -430,6 +536,48 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         int rc = harvest(h);
         if (rc != MXGEMM_OK)
             return rc;
+    }
+
+    if (P.ring == MXGEMM_RING_FLAGS) {
+        mxg::RingArgs ra;
+        ra.a_seg = (const uint8_t*)a_seg;
+        ra.sa_seg = (const uint8_t*)a_scale;
+        ra.ring = h->ring;
+        ra.sring = h->sring;
+        ra.b = (const uint8_t*)b;
+        ra.bs = (const uint8_t*)b_scale;
+        ra.c = (uint16_t*)c;
+        ra.ws = h->ws;
+        ra.sync = h->sync;
+        ra.err = h->sync + mxg::ring_sync_words(P.window_slots, P.split, P.windows, P.tiles_m,
+                                                P.tiles_n);
+        ra.M = P.M;
+        ra.kpr = P.kPerRank;
+        ra.cms = P.commMSize;
+        ra.slot_bytes = P.slot_bytes;
+        ra.scale_slot_bytes = P.scale_slot_bytes;
+        ra.R = P.rank_size;
+        ra.N = (int)P.N;
+        ra.K = (int)P.K;
+        ra.nbuf = P.buffer_count;
+        ra.chunks = P.chunks;
+        ra.W = P.chunks_per_window;
+        ra.windows = P.windows;
+        ra.window_slots = P.window_slots;
+        ra.tiles_n = P.tiles_n;
+        ra.split = P.split;
+        ra.segs_per_split = P.rank_size / P.split;
+        ra.tiles_m_win = P.tiles_m;
+        ra.c_vec4 = ((uintptr_t)c % 8 == 0) && (P.N % 4 == 0);
+        ra.spin_limit = P.spin_limit;
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->gemm_ev[0], st));
+        HIP_TRY(mxg::launch_ring(ra, P.a_format, P.b_format, st));
+        if (h->profiling) {
+            HIP_TRY(hipEventRecord(h->gemm_ev[1], st));
+            h->pending = true;
+        }
+        return MXGEMM_OK;
     }
 
     // fork: the side stream starts after everything already on `stream`
@@ -514,6 +662,26 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
     }
     if (h->profiling)
         h->pending = true;
+    return MXGEMM_OK;
+}
+
+int mxgemm_seg_status(mxgemm_seg_t h)
+{
+    if (!h)
+        return fail(MXGEMM_EINVAL, "NULL handle");
+    if (h->plan.ring != MXGEMM_RING_FLAGS)
+        return MXGEMM_OK;
+    const mxgemm_seg_plan_t& P = h->plan;
+    uint32_t* err = h->sync + mxg::ring_sync_words(P.window_slots, P.split, P.windows, P.tiles_m,
+                                                   P.tiles_n);
+    uint32_t v = 0;
+    HIP_TRY(hipDeviceSynchronize());
+    HIP_TRY(hipMemcpy(&v, err, 4, hipMemcpyDeviceToHost));
+    if (v != 0) {
+        HIP_TRY(hipMemset(err, 0, 4));
+        HIP_TRY(hipDeviceSynchronize());
+        return fail(MXGEMM_ETIMEOUT, "a device wait of the flags protocol gave up");
+    }
     return MXGEMM_OK;
 }
 

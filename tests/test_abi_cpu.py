@@ -69,6 +69,29 @@ def test_plan_chunk_tail():
     assert p.chunks == 1
 
 
+def test_plan_flags_protocol():
+    """Device-flag ring: chosen on request where it fits (K range of a split
+    <= 8 K-steps, one work-group per CU), refused where it does not."""
+    p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(ring="flags"))
+    assert p.ring == pkg.RING_FLAGS
+    assert (p.tile_m, p.tile_n, p.split, p.tiles_n, p.grid) == (32, 64, 8, 32, 256)
+    assert p.workspace_bytes == 8 * 64 * 2048 * 4
+    p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(ring="flags", chunks_per_window=4))
+    assert (p.chunks_per_window, p.windows, p.window_slots) == (4, 2, 1)
+    p = pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(ring="events"))
+    assert p.ring == pkg.RING_EVENTS
+    for bad in (dict(ring="flags", precision=pkg.PRECISION_NATIVE), dict(ring="flags", tile_cfg=1)):
+        with pytest.raises(pkg.MxgemmError):
+            pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(**bad))
+    with pytest.raises(pkg.MxgemmError):          # K range of every split > 8 K-steps
+        pkg.plan(4096, 896, 8, 4096, 512, 4, opts=pkg.options(ring="flags"))
+    with pytest.raises(pkg.MxgemmError):
+        pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(ring=5))
+    p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(ring="flags"))
+    with pytest.raises(pkg.MxgemmError):          # no work-ID decoding for flags plans
+        pkg.decode(p, 16, 0, 0)
+
+
 def test_plan_formats():
     p = pkg.plan(128, 256, 2, 256, 64, 2)
     assert (p.a_format, p.b_format) == (pkg.FMT_E4M3, pkg.FMT_E4M3)
