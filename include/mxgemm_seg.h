@@ -183,8 +183,10 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
  * only after its copy (ready event) and a slot is refilled only after the
  * GEMM that read it (credit event) -- the ready/credit pairing of
  * MatmulProcess / AllToAllProcess.  With S > 1 a window's GEMM writes FP32
- * partials into the handle's workspace and a second kernel on `stream` sums
- * them in split order into C (the result does not depend on timing).  The
+ * partials into the handle's workspace and they are summed in split order
+ * into C (the result does not depend on timing): by the last split of each
+ * tile to finish, inside the GEMM launch, when a tile's partials of all
+ * splits take at most 128 KiB, else by a second kernel on `stream`.  The
  * side stream forks from and joins
  * back into `stream`, so work before and after run() on `stream` stays
  * ordered and the call can be captured into a HIP graph.  A handle must not

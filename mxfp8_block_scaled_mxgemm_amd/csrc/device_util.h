@@ -95,6 +95,119 @@ __device__ __forceinline__ void dma4(const void* g, void* lds)
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// ---- data one work-group writes for another in the same launch ----------
+// Each XCD has its own L2, so such data is written with device-scope stores
+// (SC1: written through to the memory side) and read with device-scope
+// loads (SC1: a stale L2 line is not used), and a counter is raised only
+// once the writer's stores have completed (stores_done).  This avoids the
+// agent-wide release / acquire fences, which write back or invalidate a
+// whole L2.
+
+// 4-byte device-scope store (a relaxed agent-scope atomic store).
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p)
+{
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16-byte device-scope store (global_store_dwordx4 with SC1; its data is
+// read at issue).  The compiler does not count it: stores_done() waits.
+__device__ __forceinline__ void st_dev16(void* p, const u32x4& v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+
+// Eight 16-byte device-scope loads and the wait for them in one statement,
+// so no use of a result can be placed before the data has arrived.
+__device__ __forceinline__ void ld_dev16x8(const void* const (&p)[8], u32x4 (&v)[8])
+{
+    asm volatile(
+        "global_load_dwordx4 %0, %8, off sc1\n\t"
+        "global_load_dwordx4 %1, %9, off sc1\n\t"
+        "global_load_dwordx4 %2, %10, off sc1\n\t"
+        "global_load_dwordx4 %3, %11, off sc1\n\t"
+        "global_load_dwordx4 %4, %12, off sc1\n\t"
+        "global_load_dwordx4 %5, %13, off sc1\n\t"
+        "global_load_dwordx4 %6, %14, off sc1\n\t"
+        "global_load_dwordx4 %7, %15, off sc1\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+        : "memory");
+}
+
+// Until this thread's stores (and atomics) have completed.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Split-K combine of one tile by one work-group: for the tile's valid rows
+// r < nrows and columns col0 + cc < N (cc < tile_n),
+//   c[(row0 + r) N + col0 + cc] = bf16(sum over t = 0 .. split - 1, in order,
+//                                      of ws[t plane + (row0 + r) N + col0 + cc]),
+// the partials read with device-scope loads, eight splits at a time, four
+// columns per thread.
+__device__ inline void combine_tile(const float* ws, int64_t plane, uint16_t* c, int64_t row0,
+                                    int nrows, int col0, int tile_n, int N, int split, bool c_vec4)
+{
+    for (int e = threadIdx.x * 4; e < nrows * tile_n; e += blockDim.x * 4) {
+        const int r = e / tile_n, cc = e - r * tile_n;
+        const int col = col0 + cc;
+        if (col >= N)
+            continue;
+        const int64_t idx = (row0 + r) * N + col;
+        const int nv = (N & 3) == 0 ? 4 : (N - col < 4 ? N - col : 4);
+        v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int t0 = 0; t0 < split; t0 += 8) {
+            v4f part[8];
+            if (nv == 4 && (N & 3) == 0) {
+                // splits past the last read split 0 again (ignored)
+                const void* src[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    src[i] = ws + (t0 + i < split ? (int64_t)(t0 + i) * plane : 0) + idx;
+                u32x4 raw[8];
+                ld_dev16x8(src, raw);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    part[i] = __builtin_bit_cast(v4f, raw[i]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    part[i] = v4f{0.f, 0.f, 0.f, 0.f};
+                    if (t0 + i < split)
+                        for (int v = 0; v < nv; ++v)
+                            part[i][v] = ld_dev(ws + (int64_t)(t0 + i) * plane + idx + v);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (t0 + i < split) {
+                    if (t0 + i == 0) {
+                        sum = part[i];
+                    } else {
+                        sum[0] += part[i][0];
+                        sum[1] += part[i][1];
+                        sum[2] += part[i][2];
+                        sum[3] += part[i][3];
+                    }
+                }
+        }
+        if (nv == 4 && c_vec4) {
+            *reinterpret_cast<u32x2*>(c + idx) = u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+        } else {
+            for (int v = 0; v < nv; ++v)
+                c[idx + v] = f32_to_bf16_rne(sum[v]);
+        }
+    }
+}
+
 template <int MW>
 struct AccT;
 template <>

@@ -219,7 +219,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoord& t
                 const int64_t off = lane_base + (int64_t)(i * MW) * p.N + cofs;
                 const v4f x = v4f{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 if (vec && col + 3 < p.N) {
-                    if (partial)
+                    if (partial && p.fused)
+                        st_dev16(wsp + off, __builtin_bit_cast(u32x4, x));
+                    else if (partial)
                         *reinterpret_cast<v4f*>(wsp + off) = x;
                     else
                         *reinterpret_cast<u32x2*>(p.c + off) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
@@ -227,7 +229,9 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoord& t
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
                         if (col + u < p.N) {
-                            if (partial)
+                            if (partial && p.fused)
+                                st_dev(wsp + off + u, x[u]);
+                            else if (partial)
                                 wsp[off + u] = x[u];
                             else
                                 p.c[off + u] = f32_to_bf16_rne(x[u]);
@@ -235,6 +239,31 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoord& t
                 }
             }
     }
+}
+
+// Split-K, fused combine: once this work-group's partials are stored
+// (device-scope), count its arrival at the tile; the last split to arrive
+// sums the tile's partials in split order into C and sets the count back to
+// zero for the next launch.  Nothing waits, so the grid need not be
+// resident at once.
+template <int BM, int BN>
+__device__ __forceinline__ void split_combine(const GemmArgs& p, const TileCoord& tc, int m0, int n0)
+{
+    __shared__ uint32_t s_last;
+    stores_done();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t* cnt = p.tile_cnt + tc.tm * p.tiles_n + tc.tn;
+        const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == (uint32_t)(p.split - 1);
+        if (s_last)
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+    const int nr = p.rows - m0 < BM ? p.rows - m0 : BM;
+    combine_tile(p.ws, (int64_t)p.rows * p.N, p.c, m0, nr, n0, BN, p.N, p.split, p.c_vec4 != 0);
 }
 
 // Block-scaled GEMM, scaled-MFMA (native) forms and the 16-wide exact form.
@@ -487,6 +516,8 @@ mxgemm_kernel(GemmArgs p)
         }
 
         store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
+        if (p.split > 1 && p.fused)
+            split_combine<BM, BN>(p, tc, m0, n0);
     }
 }
 
@@ -738,6 +769,8 @@ mxgemm_exact_kernel(GemmArgs p)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the work-group
 
         store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
+        if (p.split > 1 && p.fused)
+            split_combine<BM, BN>(p, tc, m0, n0);
     }
 }
 

@@ -45,6 +45,8 @@ struct GemmArgs {
     const uint8_t* bs;        // [N][K/32]
     uint16_t* c;              // C + first window row * N
     float* ws;                // split-K partials [split][rows][N] (split > 1)
+    uint32_t* tile_cnt;       // fused combine: arrivals per tile [tiles_m][tiles_n], zero between launches
+    int fused;                // split > 1: the last split of a tile sums the partials
     int rows, N, K, kpr, cms;
     int tiles_m, tiles_n, split, segs_per_split, group_n, total_work;
     int c_vec4;               // C rows may be written 4 elements (8 bytes) at a time

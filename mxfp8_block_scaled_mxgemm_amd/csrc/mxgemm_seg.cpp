@@ -74,6 +74,15 @@ struct Choice {
     double cost;
 };
 
+// Split-K combine inside the GEMM launch (the last split of a tile sums the
+// partials) when one work-group's share is small: the tile's partials of
+// all splits at most 128 KiB.  Larger tiles use a separate reduce kernel
+// spread over the whole device.
+bool fused_combine(int tile_m, int tile_n, int split)
+{
+    return split > 1 && (int64_t)tile_m * tile_n * split * 4 <= (128 << 10);
+}
+
 // Estimated time of one window under (cfg, split), in 2.4 GHz clocks.  A
 // work item is bound either by its MFMAs (at the tile's efficiency, shared
 // with the other resident work-groups of the CU) or by the round trips of
@@ -96,10 +105,16 @@ double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int s
     const double item = (compute > copy ? compute : copy) + 3000.0;
     double total = (double)rounds * item;
     if (split > 1) {
-        // FP32 partials written and read back, C written, by a second
-        // launch: bytes at ~2.5 TB/s (measured), plus the launch
-        const double bytes = (double)rows * N * (8.0 * split + 2.0);
-        total += bytes / 2.5e12 * 2.4e9 + 5000.0;
+        if (fused_combine(t.tile_m, t.tile_n, split)) {
+            // the last split of each tile reads the tile's partials (~12
+            // B/clock per CU) after a device-scope round trip
+            total += (double)t.tile_m * t.tile_n * split * 4.0 / 12.0 + 3000.0;
+        } else {
+            // FP32 partials written and read back, C written, by a second
+            // launch: bytes at ~2.5 TB/s (measured), plus the launch
+            const double bytes = (double)rows * N * (8.0 * split + 2.0);
+            total += bytes / 2.5e12 * 2.4e9 + 5000.0;
+        }
     }
     return total;
 }
@@ -318,6 +333,7 @@ struct mxgemm_seg {
     uint8_t* ring;
     uint8_t* sring;
     float* ws;
+    uint32_t* tile_cnt;   // events protocol, fused split-K combine: arrivals per tile
     uint32_t* sync;   // flags protocol: counters, then the error word
     hipStream_t side;
     hipEvent_t start;
@@ -356,6 +372,8 @@ void release(mxgemm_seg* h)
         (void)hipFree(h->ws);
     if (h->sync)
         (void)hipFree(h->sync);
+    if (h->tile_cnt)
+        (void)hipFree(h->tile_cnt);
     delete h;
 }
 
@@ -470,6 +488,16 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
         return oom("staging scale ring", sring_bytes);
     if (plan.workspace_bytes > 0 && hipMalloc((void**)&h->ws, plan.workspace_bytes) != hipSuccess)
         return oom("split-K workspace", plan.workspace_bytes);
+    if (plan.ring == MXGEMM_RING_EVENTS && fused_combine(plan.tile_m, plan.tile_n, plan.split)) {
+        // arrival counts start at zero; every launch leaves them at zero
+        const size_t bytes = 4 * (size_t)plan.tiles_m * plan.tiles_n;
+        if (hipMalloc((void**)&h->tile_cnt, bytes) != hipSuccess)
+            return oom("split-K tile counters", bytes);
+        if (hipMemset(h->tile_cnt, 0, bytes) != hipSuccess) {
+            release(h);
+            return fail(MXGEMM_EHIP, "clearing the split-K tile counters failed");
+        }
+    }
     if (plan.ring == MXGEMM_RING_FLAGS) {
         // counters start at zero; each run leaves them at zero
         const size_t bytes = 4 * (size_t)(mxg::ring_sync_words(plan.window_slots, plan.split,
@@ -630,6 +658,8 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         ga.bs = (const uint8_t*)b_scale;
         ga.c = (uint16_t*)c + (int64_t)chunk0 * P.commMSize * P.N;
         ga.ws = h->ws;
+        ga.tile_cnt = h->tile_cnt;
+        ga.fused = fused_combine(P.tile_m, P.tile_n, P.split) ? 1 : 0;
         ga.rows = (int)rows;
         ga.N = (int)P.N;
         ga.K = (int)P.K;
@@ -648,7 +678,7 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
                                  P.b_format, ga, st));
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
-        if (P.split > 1) {
+        if (P.split > 1 && !ga.fused) {
             mxg::ReduceArgs ra;
             ra.ws = h->ws;
             ra.c = ga.c;

@@ -52,43 +52,6 @@ constexpr int kRedRow = 68;
 // Cache-policy operand of global_load_lds: SC1, device scope.
 constexpr int kDeviceScope = 16;
 
-// Device-scope (write-through) 4-byte store, as a relaxed agent-scope
-// atomic.
-__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// 16-byte device-scope store (global_store_dwordx4 with SC1; its data is
-// read at issue).  The compiler does not count it: stores_done() waits.
-__device__ __forceinline__ void st_dev16(void* p, const u32x4& v)
-{
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
-
-// Eight 16-byte device-scope loads and the wait for them in one statement,
-// so no use of a result can be placed before the data has arrived.
-__device__ __forceinline__ void ld_dev16x8(const void* const (&p)[8], u32x4 (&v)[8])
-{
-    asm volatile(
-        "global_load_dwordx4 %0, %8, off sc1\n\t"
-        "global_load_dwordx4 %1, %9, off sc1\n\t"
-        "global_load_dwordx4 %2, %10, off sc1\n\t"
-        "global_load_dwordx4 %3, %11, off sc1\n\t"
-        "global_load_dwordx4 %4, %12, off sc1\n\t"
-        "global_load_dwordx4 %5, %13, off sc1\n\t"
-        "global_load_dwordx4 %6, %14, off sc1\n\t"
-        "global_load_dwordx4 %7, %15, off sc1\n\t"
-        "s_waitcnt vmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
-          "=&v"(v[6]), "=&v"(v[7])
-        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
-        : "memory");
-}
-
-// Until this thread's stores (and atomics) have completed.
-__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Thread 0 polls *ptr (device-scope loads) until it reaches `target` or
 // gives up; the barrier holds the work-group until then, so its later
 // device-scope loads see what the count's writers stored before raising it.
@@ -423,8 +386,7 @@ __global__ void __launch_bounds__(NT) ring_kernel(RingArgs p)
 #pragma unroll
                             for (int v = 0; v < 4; ++v)
                                 if (col + v < p.N)
-                                    __hip_atomic_store(dp + v, o[h][v], __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
+                                    st_dev(dp + v, o[h][v]);
                         }
                     }
                 }
@@ -437,64 +399,10 @@ __global__ void __launch_bounds__(NT) ring_kernel(RingArgs p)
                 __syncthreads();
                 if (bcast == (uint32_t)(p.split - 1)) {
                     // last split of this tile: C = bf16(sum of the partials
-                    // in split order), four columns per thread; the
-                    // partials are loaded eight splits at a time, all
-                    // loads in flight together, then added in order
-                    for (int e = tid * 4; e < BM * BN; e += NT * 4) {
-                        const int r = e / BN, cc = e % BN;
-                        const int wr2 = tm * BM + r;
-                        const int col = n0 + cc;
-                        if (wr2 >= rows_w || col >= p.N)
-                            continue;
-                        const int64_t idx = (row_base + wr2) * p.N + col;
-                        const int64_t plane = p.M * p.N;
-                        const int nv = (p.N & 3) == 0 ? 4 : (p.N - col < 4 ? p.N - col : 4);
-                        v4f sum = v4f{0.f, 0.f, 0.f, 0.f};
-                        for (int t0 = 0; t0 < p.split; t0 += 8) {
-                            v4f part[8];
-                            if (nv == 4) {
-                                // splits past the last read split 0 again (ignored)
-                                const void* src[8];
-#pragma unroll
-                                for (int i = 0; i < 8; ++i)
-                                    src[i] = p.ws + (t0 + i < p.split ? (int64_t)(t0 + i) * plane : 0) + idx;
-                                u32x4 raw[8];
-                                ld_dev16x8(src, raw);
-#pragma unroll
-                                for (int i = 0; i < 8; ++i)
-                                    part[i] = __builtin_bit_cast(v4f, raw[i]);
-                            } else {
-#pragma unroll
-                                for (int i = 0; i < 8; ++i) {
-                                    part[i] = v4f{0.f, 0.f, 0.f, 0.f};
-                                    if (t0 + i < p.split)
-                                        for (int v = 0; v < nv; ++v)
-                                            part[i][v] = __hip_atomic_load(
-                                                p.ws + (int64_t)(t0 + i) * plane + idx + v,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                                }
-                            }
-#pragma unroll
-                            for (int i = 0; i < 8; ++i)
-                                if (t0 + i < p.split) {
-                                    if (t0 + i == 0) {
-                                        sum = part[i];
-                                    } else {
-                                        sum[0] += part[i][0];
-                                        sum[1] += part[i][1];
-                                        sum[2] += part[i][2];
-                                        sum[3] += part[i][3];
-                                    }
-                                }
-                        }
-                        if (nv == 4 && p.c_vec4) {
-                            *reinterpret_cast<u32x2*>(p.c + idx) =
-                                u32x2{pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
-                        } else {
-                            for (int v = 0; v < nv; ++v)
-                                p.c[idx + v] = f32_to_bf16_rne(sum[v]);
-                        }
-                    }
+                    // in split order)
+                    const int nr = rows_w - tm * BM < BM ? rows_w - tm * BM : BM;
+                    combine_tile(p.ws, p.M * p.N, p.c, row_base + tm * BM, nr, n0, BN, p.N,
+                                 p.split, p.c_vec4 != 0);
                 }
             }
             __syncthreads();   // the next tile row reuses lds_a
