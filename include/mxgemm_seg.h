@@ -178,17 +178,21 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
  * offsets r*M*rowBytes + mOffset*rowBytes), all_to_all_matmul.cpp (host
  * buffer sizes), all_to_all_matmul_impl.h (TransB = true, C offset
  * mOffset * N).  Chunk j (rows [j*commMSize, min((j+1)*commMSize, M)) of every
- * segment, with their scales) is copied by a staging kernel on the handle's
- * side stream into ring slot j % buffer_count; the GEMM for a chunk starts
- * only after its copy (ready event) and a slot is refilled only after the
- * GEMM that read it (credit event) -- the ready/credit pairing of
- * MatmulProcess / AllToAllProcess.  With S > 1 a window's GEMM writes FP32
+ * segment, with their scales) is copied by a staging kernel into ring slot
+ * j % buffer_count; the GEMM for a chunk starts only after its copy (ready)
+ * and a slot is refilled only after the GEMM that read it (credit) -- the
+ * ready/credit pairing of MatmulProcess / AllToAllProcess.  With two or
+ * more slot groups (buffer_count / W >= 2) the staging runs ahead on the
+ * handle's side stream, paired with the GEMMs by ready and credit events;
+ * with one slot group it could not run ahead, and both kernels run in
+ * order on `stream`.  With S > 1 a window's GEMM writes FP32
  * partials into the handle's workspace and they are summed in split order
  * into C (the result does not depend on timing): by the last split of each
  * tile to finish, inside the GEMM launch, when a tile's partials of all
  * splits take at most 128 KiB, else by a second kernel on `stream`.  The
- * side stream forks from and joins
- * back into `stream`, so work before and after run() on `stream` stays
+ * side stream, when used, forks from and joins back into `stream`; with the
+ * flags protocol everything is one launch on `stream`.  Work before and
+ * after run() on `stream` therefore stays
  * ordered and the call can be captured into a HIP graph.  A handle must not
  * be run concurrently on two streams; distinct handles may.
  * Errors: EINVAL (NULL handle/pointer, misaligned pointer), EHIP.
@@ -262,9 +266,10 @@ int mxgemm_quantize_mx(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
 
 /*
  * Kernel timing for measurement.  While enabled, run() brackets every GEMM
- * kernel launch (on `stream`; with S > 1 the split-K reduction after it is
- * outside the bracket) and every staging launch (on the side stream) with
- * timing events.  mxgemm_seg_kernel_times synchronises the handle and
+ * kernel launch (on `stream`; a separate split-K reduce kernel after it is
+ * outside the bracket, a fused combine inside) and every staging launch
+ * (on the stream it runs on) with timing events; the flags protocol's one
+ * launch counts as a GEMM launch.  mxgemm_seg_kernel_times synchronises the handle and
  * returns the summed durations (ms) and launch counts since the last call,
  * then resets them.  Not for use under graph capture.  Errors: EINVAL, EHIP.
  */

@@ -608,9 +608,18 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         return MXGEMM_OK;
     }
 
-    // fork: the side stream starts after everything already on `stream`
-    HIP_TRY(hipEventRecord(h->start, st));
-    HIP_TRY(hipStreamWaitEvent(h->side, h->start, 0));
+    // With one slot group the staging of a window waits for the GEMM of the
+    // previous one anyway: both run on `stream`, whose order is then the
+    // ready/credit order (no cross-stream hand-offs, each of which costs
+    // tens of microseconds between these kernels).  Otherwise the staging
+    // runs on the side stream, forked from `stream`, so that it can run
+    // ahead of the GEMMs.
+    const bool one_stream = P.window_slots == 1;
+    hipStream_t producer = one_stream ? st : h->side;
+    if (!one_stream) {
+        HIP_TRY(hipEventRecord(h->start, st));
+        HIP_TRY(hipStreamWaitEvent(h->side, h->start, 0));
+    }
 
     for (int w = 0; w < P.windows; ++w) {
         const int chunk0 = w * P.chunks_per_window;
@@ -619,7 +628,7 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         const int g = w % P.window_slots;
 
         // producer: refill slot group g once the GEMM that last read it is done
-        if (w >= P.window_slots)
+        if (!one_stream && w >= P.window_slots)
             HIP_TRY(hipStreamWaitEvent(h->side, h->credit[g], 0));
         mxg::StageArgs sa;
         sa.a_seg = (const uint8_t*)a_seg;
@@ -636,14 +645,15 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         sa.nch = nch;
         sa.nbuf = P.buffer_count;
         if (h->profiling)
-            HIP_TRY(hipEventRecord(h->stage_ev[2 * w], h->side));
-        HIP_TRY(mxg::launch_stage(sa, h->side));
+            HIP_TRY(hipEventRecord(h->stage_ev[2 * w], producer));
+        HIP_TRY(mxg::launch_stage(sa, producer));
         if (h->profiling)
-            HIP_TRY(hipEventRecord(h->stage_ev[2 * w + 1], h->side));
-        HIP_TRY(hipEventRecord(h->ready[g], h->side));
-
-        // consumer: GEMM over the window once its chunks have landed
-        HIP_TRY(hipStreamWaitEvent(st, h->ready[g], 0));
+            HIP_TRY(hipEventRecord(h->stage_ev[2 * w + 1], producer));
+        if (!one_stream) {
+            HIP_TRY(hipEventRecord(h->ready[g], h->side));
+            // consumer: GEMM over the window once its chunks have landed
+            HIP_TRY(hipStreamWaitEvent(st, h->ready[g], 0));
+        }
         // rows of the window: whole chunks, except that the last chunk of
         // the problem holds only the rows left
         const int64_t rows_left = P.M - (int64_t)chunk0 * P.commMSize;
@@ -688,7 +698,8 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
             ra.c_vec4 = ga.c_vec4;
             HIP_TRY(mxg::launch_reduce(ra, st));
         }
-        HIP_TRY(hipEventRecord(h->credit[g], st));
+        if (!one_stream)
+            HIP_TRY(hipEventRecord(h->credit[g], st));
     }
     if (h->profiling)
         h->pending = true;
