@@ -138,9 +138,16 @@ def cpu_baseline(w, target_s: float):
     oracle.mxgemm_seg_rows(a_seg, s_seg, qb, sb, 0, rows)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"rows [0, {rows}) of C = {rows}x{w.N} outputs at K={w.K} "
-                      f"(dequantise + double-precision dot + bfloat16 rounding), {dt:.1f} s"}
+                      f"(dequantise + double-precision dot + bfloat16 rounding), {dt:.1f} s "
+                      f"on {threads} threads of {cpu}"}
 
 
 def main():
