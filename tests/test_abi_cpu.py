@@ -5,6 +5,8 @@ import os
 import re
 
 import numpy as np
+import ctypes
+
 import pytest
 
 import mxfp8_block_scaled_mxgemm_amd as pkg
@@ -90,6 +92,17 @@ def test_plan_flags_protocol():
     p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(ring="flags"))
     with pytest.raises(pkg.MxgemmError):          # no work-ID decoding for flags plans
         pkg.decode(p, 16, 0, 0)
+
+
+def test_quantizer_rejects_unknown_format_before_touching_memory():
+    """The format and shape rules are checked on the host first (NULL
+    pointers are never dereferenced here)."""
+    lib = pkg.load()
+    vp = ctypes.c_void_p
+    rc = lib.mxgemm_quantize_mx(vp(0), 4, 64, 64, vp(0), 64, vp(0), 2, 2, vp(0))
+    assert rc == pkg._lib.MXGEMM_EINVAL and b"format" in lib.mxgemm_seg_last_error()
+    rc = lib.mxgemm_quantize_mx(vp(0), 4, 64, 64, vp(0), 64, vp(0), 2, 0, vp(0))
+    assert rc == pkg._lib.MXGEMM_EINVAL           # NULL pointers
 
 
 def test_plan_formats():
