@@ -18,8 +18,9 @@
  *
  *   C[m, n] = sum_{r<R} sum_{k<kPerRank} A_r[m, k] * B[n, r*kPerRank + k]
  *
- * with every operand MXFP8: FP8 E4M3 (OCP "FN") codes plus one E8M0 scale
- * byte per 32 consecutive K-elements, value = e4m3(q) * 2^(scale - 127).
+ * with every operand MXFP8: FP8 codes (E4M3, OCP "FN", by default; E5M2 on
+ * request, per operand) plus one E8M0 scale byte per 32 consecutive
+ * K-elements, value = fp8(q) * 2^(scale - 127).
  * Products accumulate in FP32 over all segments (all_to_all_matmul_impl.h,
  * SetupParams: splitKNum = rankSize) and C is written as bfloat16 with
  * round-to-nearest-even.  On one GPU the R ranks are simulated: all R
@@ -152,8 +153,9 @@ typedef struct mxgemm_seg_options {
  * 32; this build also needs kPerRank % 128 == 0 (one MFMA K-step), else
  * MXGEMM_EUNSUPPORTED.  Allocates, on the current device, the staging ring
  * (buffer_count * R * commMSize * kPerRank * 33/32 bytes), the split-K
- * workspace, a side stream at default priority and the ring's
- * events; run() allocates nothing.  Errors: EINVAL, ENOMEM, EHIP,
+ * workspace and its per-tile arrival counts, the flags protocol's counters,
+ * a side stream at default priority and the ring's events; run() allocates
+ * nothing.  Errors: EINVAL, ENOMEM, EHIP,
  * EUNSUPPORTED (device is not gfx950).  *out is set only on success.
  */
 int mxgemm_seg_create(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
