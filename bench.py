@@ -75,6 +75,7 @@ def load_traffic(workload: str, sha: str):
 SAMPLER = r"""
 import json, os, subprocess, sys, time
 out, parent = sys.argv[1], int(sys.argv[2])
+use_temp = True
 while True:
     try:
         os.kill(parent, 0)
@@ -83,14 +84,29 @@ while True:
     if os.path.exists(out + ".stop"):
         break
     try:
-        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"],
-                           capture_output=True, text=True, timeout=10)
+        cmd = ["amd-smi", "metric", "-g", "0", "--clock", "--power", "--json"]
+        if use_temp:
+            cmd.insert(-1, "--temperature")
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=10)
+        if r.returncode != 0 and use_temp:
+            use_temp = False
+            continue
         g = json.loads(r.stdout)["gpu_data"][0]
+        num = lambda v: v if isinstance(v, (int, float)) else None
         clk = [v["clk"]["value"] for k, v in g["clock"].items()
                if k.startswith("gfx_") and isinstance(v.get("clk", {}).get("value"), (int, float))]
+        mem = num(((g["clock"].get("mem_0") or {}).get("clk") or {}).get("value"))
         pw = g["power"]["socket_power"]["value"]
+        temp = None
+        for key in ("hotspot", "edge"):
+            t = (g.get("temperature") or {}).get(key)
+            t = t.get("value") if isinstance(t, dict) else t
+            if num(t) is not None:
+                temp = t
+                break
         with open(out, "a") as f:
-            f.write(json.dumps({"t": time.time(), "gfx_mhz": clk, "power_w": pw}) + "\n")
+            f.write(json.dumps({"t": time.time(), "gfx_mhz": clk, "power_w": pw, "mem_mhz": mem,
+                                "temp_c": temp}) + "\n")
     except Exception:
         time.sleep(0.5)
     time.sleep(0.1)
@@ -323,8 +339,12 @@ def main():
             telemetry = {"samples": len(rows), "shader_clock_mhz_median": round(statistics.median(mhz), 1),
                          "shader_clock_mhz_min": round(min(mhz), 1),
                          "socket_power_w_median": round(statistics.median(r["power_w"] for r in rows), 1),
-                         "source": "amd-smi metric --clock --power, mean over XCDs, during "
-                                   f"{t1 - t0:.1f} s of back-to-back steps (no flush)"}
+                         "source": "amd-smi metric --clock --power (--temperature), mean over XCDs, "
+                                   f"during {t1 - t0:.1f} s of back-to-back steps (no flush)"}
+            for key, name in (("mem_mhz", "memory_clock_mhz_median"), ("temp_c", "temperature_c_median")):
+                vals = [r[key] for r in rows if r.get(key) is not None]
+                if vals:
+                    telemetry[name] = round(statistics.median(vals), 1)
             log(f"[bench] telemetry: {telemetry}")
     if graph is not None:
         del graph
