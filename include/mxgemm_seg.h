@@ -88,7 +88,7 @@ enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
  *    split), polled with agent-scope acquire and released with agent-scope
  *    release.  The last split to finish a tile sums the FP32 partials in
  *    split order.  One launch and one read of B instead of one per window:
- *    for short M (skinny shapes).  Exact precision only.  All work-groups
+ *    for short M (skinny shapes).  Both precision modes.  All work-groups
  *    must be resident at once (at most one per compute unit); a wait that
  *    polls spin_limit times without progress gives up, marks the handle
  *    (mxgemm_seg_status) and lets the kernel finish, so a run never hangs.

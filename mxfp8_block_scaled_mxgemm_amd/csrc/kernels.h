@@ -103,7 +103,7 @@ __host__ __device__ inline int64_t ring_sync_words(int window_slots, int split, 
     return 2LL * window_slots * split + (int64_t)windows * tiles_m_win * tiles_n + 1;
 }
 
-hipError_t launch_ring(const RingArgs& a, int fa, int fb, hipStream_t stream);
+hipError_t launch_ring(const RingArgs& a, int fa, int fb, bool exact, hipStream_t stream);
 
 hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 // One work-group per work item (a.total_work of them); fa, fb: the FP8

@@ -285,7 +285,7 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     if (want == MXGEMM_RING_EVENTS)
         return MXGEMM_OK;
     const bool forced_tiles = opts && (opts->tile_cfg >= 0 || opts->split > 0);
-    int s = exact && !forced_tiles ? ring_split(kpr, R, N, num_cus) : 0;
+    int s = !forced_tiles ? ring_split(kpr, R, N, num_cus) : 0;
     const int Wr = opts && opts->chunks_per_window > 0 ? opts->chunks_per_window
                                                        : (nbuf > 1 ? nbuf / 2 : 1);
     const int64_t windows_r = ceil_div(p->chunks, Wr);
@@ -300,9 +300,9 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     }
     if (s == 0) {
         if (want == MXGEMM_RING_FLAGS)
-            return fail(MXGEMM_EUNSUPPORTED, "the flags protocol needs exact precision, no forced "
-                        "tile or split, a split whose K range is at most %d K-steps of 128 and at "
-                        "most one work-group per compute unit (%d)", mxg::kRingMaxSteps, num_cus);
+            return fail(MXGEMM_EUNSUPPORTED, "the flags protocol needs no forced tile or split, a "
+                        "split whose K range is at most %d K-steps of 128 and at most one "
+                        "work-group per compute unit (%d)", mxg::kRingMaxSteps, num_cus);
         return MXGEMM_OK;
     }
     const double ring_cost = estimate_ring(M, kpr, R, s, (int)windows_r, (int)tiles_m_win);
@@ -600,7 +600,7 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         ra.spin_limit = P.spin_limit;
         if (h->profiling)
             HIP_TRY(hipEventRecord(h->gemm_ev[0], st));
-        HIP_TRY(mxg::launch_ring(ra, P.a_format, P.b_format, st));
+        HIP_TRY(mxg::launch_ring(ra, P.a_format, P.b_format, P.precision == MXGEMM_PRECISION_EXACT, st));
         if (h->profiling) {
             HIP_TRY(hipEventRecord(h->gemm_ev[1], st));
             h->pending = true;

@@ -170,7 +170,7 @@ __device__ void stage_share(const RingArgs& p, int chunk0, int nch, int seg0, in
 
 }  // namespace
 
-template <int FA, int FB>
+template <int FA, int FB, bool EXACT>
 __global__ void __launch_bounds__(NT) ring_kernel(RingArgs p)
 {
     // LDS: the B tile for the whole run and one A tile, K-step by K-step
@@ -295,6 +295,38 @@ __global__ void __launch_bounds__(NT) ring_kernel(RingArgs p)
             for (int ks = wave; ks < nsteps; ks += 4) {
                 const uint8_t* pa = lds_a + ks * A_STEP + lr * kBK;
                 const uint8_t* pb = lds_b + ks * B_STEP + lr * kBK;
+                if constexpr (!EXACT) {
+                    // Native: one v_mfma_scale_f32_16x16x128_f8f6f4 per block
+                    // and K-step; lane group q holds K [16q, 16q + 16) and
+                    // [64 + 16q, +16) (chunks q and q + 4) and the scale
+                    // byte of MX block q.
+                    const int off_lo = swz(lr, lq) * 16, off_hi = swz(lr, lq + 4) * 16;
+                    v8i af[2], bf[4];
+                    int sav[2], sbv[4];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const u32x4 lo = *reinterpret_cast<const u32x4*>(pa + i * 16 * kBK + off_lo);
+                        const u32x4 hi = *reinterpret_cast<const u32x4*>(pa + i * 16 * kBK + off_hi);
+                        af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                    (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        sav[i] = lds_sa[ks * 256 + (i * 16 + lr) * 4 + lq];
+                    }
+#pragma unroll
+                    for (int gb = 0; gb < 4; ++gb) {
+                        const u32x4 lo = *reinterpret_cast<const u32x4*>(pb + gb * 16 * kBK + off_lo);
+                        const u32x4 hi = *reinterpret_cast<const u32x4*>(pb + gb * 16 * kBK + off_hi);
+                        bf[gb] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                        sbv[gb] = lds_sb[ks * 256 + (gb * 16 + lr) * 4 + lq];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 2; ++i)
+#pragma unroll
+                        for (int gb = 0; gb < 4; ++gb)
+                            acc[i][gb][0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                                bf[gb], af[i], acc[i][gb][0], FB, FA, 0, sbv[gb], 0, sav[i]);
+                    continue;
+                }
                 uint32_t sa_w[2], sb_w[4];
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
@@ -460,20 +492,26 @@ __global__ void __launch_bounds__(NT) ring_kernel(RingArgs p)
     }
 }
 
-hipError_t launch_ring(const RingArgs& a, int fa, int fb, hipStream_t stream)
+template <bool EXACT>
+static hipError_t launch_ring_prec(const RingArgs& a, int fa, int fb, hipStream_t stream)
 {
     const dim3 grid((unsigned)(a.tiles_n * a.split)), block(NT);
     if (fa == kE4M3 && fb == kE4M3)
-        hipLaunchKernelGGL((ring_kernel<kE4M3, kE4M3>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ring_kernel<kE4M3, kE4M3, EXACT>), grid, block, 0, stream, a);
     else if (fa == kE5M2 && fb == kE5M2)
-        hipLaunchKernelGGL((ring_kernel<kE5M2, kE5M2>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ring_kernel<kE5M2, kE5M2, EXACT>), grid, block, 0, stream, a);
     else if (fa == kE4M3 && fb == kE5M2)
-        hipLaunchKernelGGL((ring_kernel<kE4M3, kE5M2>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ring_kernel<kE4M3, kE5M2, EXACT>), grid, block, 0, stream, a);
     else if (fa == kE5M2 && fb == kE4M3)
-        hipLaunchKernelGGL((ring_kernel<kE5M2, kE4M3>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((ring_kernel<kE5M2, kE4M3, EXACT>), grid, block, 0, stream, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+hipError_t launch_ring(const RingArgs& a, int fa, int fb, bool exact, hipStream_t stream)
+{
+    return exact ? launch_ring_prec<true>(a, fa, fb, stream) : launch_ring_prec<false>(a, fa, fb, stream);
 }
 
 }  // namespace mxg

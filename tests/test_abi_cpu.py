@@ -82,7 +82,9 @@ def test_plan_flags_protocol():
     assert (p.chunks_per_window, p.windows, p.window_slots) == (4, 2, 1)
     p = pkg.plan(128, 256, 2, 256, 64, 2, opts=pkg.options(ring="events"))
     assert p.ring == pkg.RING_EVENTS
-    for bad in (dict(ring="flags", precision=pkg.PRECISION_NATIVE), dict(ring="flags", tile_cfg=1)):
+    p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(ring="flags", precision=pkg.PRECISION_NATIVE))
+    assert p.ring == pkg.RING_FLAGS and p.precision == pkg.PRECISION_NATIVE
+    for bad in (dict(ring="flags", tile_cfg=1), dict(ring="flags", split=4)):
         with pytest.raises(pkg.MxgemmError):
             pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(**bad))
     with pytest.raises(pkg.MxgemmError):          # K range of every split > 8 K-steps

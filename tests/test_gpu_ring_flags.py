@@ -93,6 +93,44 @@ def test_flags_formats(fa, fb):
     assert not bad.any(), summary(got, ref)
 
 
+@pytest.mark.parametrize("shape", [
+    (8, 64, 896, 2048, 8, 4),       # skinny geometry
+    (2, 128, 256, 256, 64, 2),      # tiny geometry
+    (4, 130, 256, 200, 48, 2),      # tail chunk, ragged N
+    (3, 1000, 384, 520, 96, 4),     # odd R, several tile rows per window
+])
+@pytest.mark.parametrize("fa,fb", [(oracle.E4M3, oracle.E4M3), (oracle.E5M2, oracle.E4M3)])
+def test_flags_native_precision(shape, fa, fb):
+    """The flags protocol on the scaled FP8 MFMA (native precision)."""
+    torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    R, M, kpr, N, cms, nbuf = shape
+    say(f"[flags-native] R={R} M={M} kpr={kpr} N={N} cms={cms} nbuf={nbuf} fa={fa} fb={fb}")
+    case = custom_case(R=R, M=M, kpr=kpr, N=N, cms=cms, nbuf=nbuf, seed=47 + M, fmt_a=fa, fmt_b=fb)
+    got = _run_checked(case, _flags(precision=pkg.PRECISION_NATIVE))
+    ref = case.oracle_full()
+    say("  " + summary(got, ref))
+    bad, _ = within_tol(got, ref)
+    assert not bad.any()
+
+
+@pytest.mark.parametrize("precision", ["exact", "native"])
+def test_flags_integer_data_bit_exact_both_precisions(precision):
+    torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    from gpu_common import Case
+    from mxfp8_block_scaled_mxgemm_amd import inputs
+    R, M, kpr, N, cms, nbuf = 8, 64, 896, 1024, 8, 4
+    w = inputs.Workload("sign", R, M, kpr, N, cms, nbuf, 1.0, 0.0, 1.0, 0)
+    xa = inputs.sparse_sign_matrix((M, R * kpr), 0.03, 97)
+    xb = inputs.sparse_sign_matrix((N, R * kpr), 0.03, 98)
+    case = Case(w, xa, xb)
+    ref = xa.astype(np.float64) @ xb.astype(np.float64).T
+    prec = pkg.PRECISION_EXACT if precision == "exact" else pkg.PRECISION_NATIVE
+    got = _run_checked(case, _flags(precision=prec))
+    assert np.array_equal(got, ref.astype(np.float32))
+
+
 def test_flags_integer_data_bit_exact():
     torch_cuda()
     from gpu_common import Case
