@@ -6,13 +6,18 @@ staging of every chunk of every rank segment through the ring, the
 block-scaled GEMM over all windows (with split-K fix-up where planned) and
 the bfloat16 epilogue -- one ``mxgemm_seg_run`` call.  Inputs are quantised
 on the GPU before timing and are resident in HBM.  Before every timed step a
-512 MiB buffer is written to push A, B and C out of L2 and the MALL.
+512 MiB buffer is written to push A, B and C out of L2 and the MALL.  Each
+timed loop is preceded by untimed steps of the same kind: at least --warmup
+steps and --warmup-ms of GPU time.
 
 Prints ONE JSON line (rank 0 / the only rank):
-  value      = 2*M*N*K / mean step time, in TFLOP/s
-  roofline   = the GEMM kernel's algorithmic FLOP per launch / its mean launch
-               duration (HIP events around each launch, on its stream),
-               against the MI355X dense FP8 MFMA peak
+  value      = 2*M*N*K / mean step time (steps issued on the stream), in
+               TFLOP/s; the mean over replays of a HIP graph of the step is
+               reported beside it
+  roofline   = the GEMM kernel's algorithmic FLOP (or bytes, below the ridge
+               point) per launch / its mean launch duration (HIP events
+               around each launch, on its stream), against the MI355X dense
+               peak of the MFMA form it runs (or HBM)
   cpu_baseline = the CPU oracle on a bounded row sample of the same workload
 """
 from __future__ import annotations
@@ -177,7 +182,11 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=5,
+                    help="untimed steps before each timed loop (at least; see --warmup-ms)")
+    ap.add_argument("--warmup-ms", type=float, default=25.0,
+                    help="untimed GPU time before each timed loop, in steps of the same kind "
+                         "(at most 200 steps)")
     ap.add_argument("--config", default="outlier_m8192_n8192_k8192", help="workload name (default outlier_m8192_n8192_k8192)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
@@ -185,7 +194,7 @@ def main():
     ap.add_argument("--telemetry-seconds", type=float, default=2.0,
                     help="sustained replays while amd-smi samples the shader clock (0: off)")
     ap.add_argument("--no-graph", action="store_true",
-                    help="time steps issued on the stream (default: replays of one captured step)")
+                    help="skip the second timer (replays of one HIP-graph-captured step)")
     ap.add_argument("--tile-cfg", type=int, default=-1)
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--window", type=int, default=-1)
@@ -264,19 +273,59 @@ def main():
         if not args.no_flush:
             flush.fill_(1.0)
 
-    # warm-up
-    for _ in range(max(1, args.warmup)):
-        flush_caches()
-        step()
+    # warm-up: the first call is discarded; before each timed loop, the
+    # steps of that loop run untimed for at least --warmup steps and at
+    # least --warmup-ms of GPU time (at most 200 steps), so the timed steps
+    # do not start in the clock and power transient that follows an idle GPU
+    flush_caches()
+    step()
     torch.cuda.synchronize()
+    warm_log = {}
+
+    def warm_up(run_one, label):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n, spent = 0, 0.0
+        while n < 200 and (n < max(1, args.warmup) or spent < args.warmup_ms):
+            batch = max(1, min(8, 200 - n))
+            ev0.record(stream)
+            for _ in range(batch):
+                flush_caches()
+                run_one()
+            ev1.record(stream)
+            ev1.synchronize()
+            spent += ev0.elapsed_time(ev1)
+            n += batch
+        warm_log[label] = {"steps": n, "ms": round(spent, 2)}
 
     # ---- timed steps ------------------------------------------------------
-    # Each step is one run() of the whole path.  By default the step is
-    # captured once into a HIP graph and the K timed steps are replays of it
-    # (how a serving loop issues a fixed-shape call); --no-graph times steps
-    # issued on the stream.  Either way a 512 MiB fill precedes every step
-    # (outside its events) so no step starts with warm caches.
+    # Each step is one run() of the whole path, issued on the stream the way
+    # a caller of mxgemm_seg_run issues it; these K steps give `value`.  A
+    # 512 MiB fill precedes every step (outside its events) so no step starts
+    # with warm caches; the fill also keeps the host ahead of the GPU, so the
+    # steps carry no host-enqueue gaps.  The same step captured once into a
+    # HIP graph and replayed K times is timed too and reported beside it
+    # (graph_ms_per_step; --no-graph skips it).
+    def timed(run_one):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            flush_caches()
+            starts[i].record(stream)
+            run_one()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        return [s.elapsed_time(e) for s, e in zip(starts, ends)], time.perf_counter() - t0
+
+    warm_up(step, "stream")
+    ms, wall = timed(step)
+    ms_mean = statistics.mean(ms)
+    log(f"[bench] stream-issued: mean {ms_mean:.4f} ms median {statistics.median(ms):.4f} "
+        f"min {min(ms):.4f} max {max(ms):.4f}")
+
     graph = None
+    graph_ms = None
     if not args.no_graph:
         try:
             gs = torch.cuda.Stream()
@@ -286,40 +335,14 @@ def main():
                 with torch.cuda.graph(graph, stream=gs):
                     g.run(a_q, a_s, b_q, b_s, c, stream=gs)
             torch.cuda.synchronize()
-            for _ in range(max(1, args.warmup)):
-                flush_caches()
-                graph.replay()
-            torch.cuda.synchronize()
-        except Exception as e:  # report, fall back to stream issue
-            log(f"[bench] graph capture unavailable ({e}); timing stream-issued steps")
+        except Exception as e:  # report, time stream-issued steps only
+            log(f"[bench] graph capture unavailable ({e})")
             graph = None
-
-    def timed(replay):
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            flush_caches()
-            starts[i].record(stream)
-            if replay:
-                graph.replay()
-            else:
-                step()
-            ends[i].record(stream)
-        torch.cuda.synchronize()
-        return [s.elapsed_time(e) for s, e in zip(starts, ends)], time.perf_counter() - t0
-
-    ms, wall = timed(graph is not None)
-    ms_mean = statistics.mean(ms)
-    timer = "graph" if graph is not None else "stream"
-    log(f"[bench] {timer}: mean {ms_mean:.4f} ms median {statistics.median(ms):.4f} "
-        f"min {min(ms):.4f} max {max(ms):.4f}")
-    stream_ms = None
     if graph is not None:
-        sms, _ = timed(False)
-        stream_ms = statistics.mean(sms)
-        log(f"[bench] stream-issued: mean {stream_ms:.4f} ms")
+        warm_up(graph.replay, "graph")
+        gms, _ = timed(graph.replay)
+        graph_ms = statistics.mean(gms)
+        log(f"[bench] graph replays: mean {graph_ms:.4f} ms")
 
     # ---- telemetry window: sustained steps while the sampler runs --------
     telemetry = None
@@ -420,15 +443,15 @@ def main():
                                                  "windows", "grid", "ring")}},
         "pct_of_mxfp8_peak": round(100.0 * value / PEAK_FP8_TFLOPS, 2),
         "hbm_frac_end_to_end": round(w.algorithmic_bytes / (ms_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "timer": (("replays of one HIP-graph-captured step" if timer == "graph" else "stream-issued steps")
-                  + ", HIP events per step" + (", 512 MiB cache flush before each step"
-                                                 if not args.no_flush else ", warm caches")),
-        "stream_issued_ms_per_step": round(stream_ms, 5) if stream_ms is not None else None,
+        "timer": ("stream-issued steps, HIP events per step" + (", 512 MiB cache flush before each step"
+                                                                  if not args.no_flush else ", warm caches")),
+        "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
         "ms_per_step_median": round(statistics.median(ms), 5),
         "ms_per_step_min": round(min(ms), 5),
         "ms_per_step_p90": round(sorted(ms)[min(len(ms) - 1, int(0.9 * len(ms)))], 5),
         "telemetry": telemetry,
         "wall_s_timed_loop_incl_flush": round(wall, 4),
+        "warmup_run": warm_log,
         "precision": args.precision,
         "roofline": {
             "bound": "hbm" if hbm_bound else "mfma",

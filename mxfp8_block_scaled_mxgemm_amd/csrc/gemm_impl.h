@@ -241,6 +241,52 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const TileCoord& t
     }
 }
 
+// Write a wave's TM x TN accumulators (32 x 32 MFMA blocks, layout as in
+// store_tile) as bfloat16 to C through the wave's own LDS region `buf`
+// (TM * TN * 2 bytes), so that the global stores are whole rows: a store
+// instruction writes 64 / (TN / 8) rows of TN * 2 contiguous bytes instead
+// of 32 rows of 16 bytes.  In `buf` row r holds its TN / 8 16-byte chunks
+// XOR-swizzled by r, so neither the 8-byte writes (32 rows, one column
+// chunk) nor the 16-byte reads (whole rows) pile onto a few banks.  Needs C
+// 16-byte aligned with N % 8 == 0; rows and column chunks past the edge are
+// not stored.
+template <int GA, int GB, int TM, int TN>
+__device__ __forceinline__ void store_tile_lds(const GemmArgs& p, v16f (&acc)[GA][GB], uint8_t* buf,
+                                               int row0, int col0, int lane)
+{
+    constexpr int RB = TN * 2;           // bytes per row in buf
+    constexpr int CPR = TN / 8;          // 16-byte chunks per row
+    static_assert(GA * 32 == TM && GB * 32 == TN && (CPR & (CPR - 1)) == 0 && CPR <= 64,
+                  "wave tile of whole 32 x 32 blocks, a power-of-two number of row chunks");
+    const int lr = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < GA; ++i)
+#pragma unroll
+        for (int j = 0; j < GB; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // columns 32 j + 8 q + 4 h + (0..3): chunk 4 j + q, bytes 8 h..8 h + 7
+                const int r = 32 * i + lr;
+                const int c = 4 * j + q;
+                *reinterpret_cast<u32x2*>(buf + r * RB + ((c ^ (r & (CPR - 1))) * 16) + 8 * h) =
+                    u32x2{pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                          pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+            }
+    // LDS operations of one wave complete in order; the wave reads back only
+    // what it wrote itself
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    constexpr int RPI = 64 / CPR;        // rows per store instruction
+    const int cl = lane % CPR, rl = lane / CPR;
+#pragma unroll
+    for (int t = 0; t < TM / RPI; ++t) {
+        const int r = t * RPI + rl;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(buf + r * RB + ((cl ^ (r & (CPR - 1))) * 16));
+        const int grow = row0 + r, gcol = col0 + 8 * cl;
+        if (grow < p.rows && gcol < p.N)
+            *reinterpret_cast<u32x4*>(p.c + (int64_t)grow * p.N + gcol) = v;
+    }
+}
+
 // Split-K, fused combine: once this work-group's partials are stored
 // (device-scope), count its arrival at the tile; the last split to arrive
 // sums the tile's partials in split order into C and sets the count back to
@@ -768,9 +814,19 @@ mxgemm_exact_kernel(GemmArgs p)
             kstep(s, stage0, stage1);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the work-group
 
-        store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
-        if (p.split > 1 && p.fused)
-            split_combine<BM, BN>(p, tc, m0, n0);
+        if (p.split == 1 && (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && (p.N & 7) == 0) {
+            // bfloat16 C through LDS: both stages are free once every wave
+            // has passed this barrier (its copies landed, its reads done);
+            // waves 0, 1 use stage 0, waves 2, 3 stage 1
+            static_assert(NW == 4 && 2 * TM * TN * 2 <= G::STAGE, "two wave tiles of bf16 per stage");
+            __syncthreads();
+            uint8_t* buf = (wave < 2 ? stage0 : stage1) + (wave & 1) * (TM * TN * 2);
+            store_tile_lds<GA, GB, TM, TN>(p, acc, buf, m0 + wm * TM, n0 + wn * TN, lane);
+        } else {
+            store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
+            if (p.split > 1 && p.fused)
+                split_combine<BM, BN>(p, tc, m0, n0);
+        }
     }
 }
 
