@@ -373,3 +373,36 @@ def test_one_block_scale_probe_gpu(operand, precision):
             contrib = xa[:, kg0:kg0 + 32].astype(np.int64) @ xb[row, kg0:kg0 + 32].astype(np.int64)
             exp[:, row] += (2 ** t - 1) * contrib
         assert np.array_equal(got, exp), (operand, r, row, blk)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("variant", ["n_mult8", "n196", "n198", "c_offset"])
+def test_exact_large_tile_output_paths(cfg, variant):
+    """The exact large-tile kernel writes C as whole rows through LDS when C
+    is 16-byte aligned and N % 8 == 0, and with per-lane stores otherwise
+    (N = 196 or 198, or C starting 2 bytes past an aligned address).  Both
+    must store every element of C and nothing past it."""
+    torch_cuda()
+    import torch
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    N = {"n_mult8": 264, "n196": 196, "n198": 198, "c_offset": 264}[variant]
+    key = f"outpaths{N}"
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = custom_case(R=2, M=300, kpr=256, N=N, cms=100, nbuf=4, seed=41 + N)
+        _CACHE[key + "ref"] = _CACHE[key].oracle_full()
+    case, ref = _CACHE[key], _CACHE[key + "ref"]
+    say(f"[out-paths] cfg={cfg} {variant} M=300 N={N}")
+    M = 300
+    pad = 1 if variant == "c_offset" else 0
+    buf = torch.full((M * N + pad + 64,), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    c = buf[pad:pad + M * N].view(M, N)
+    if variant == "c_offset":
+        assert c.data_ptr() % 16 == 2
+    got = case.run_gpu(opts=pkg.options(tile_cfg=cfg, split=1), c=c).float().cpu().numpy()
+    bad, _ = within_tol(got, ref)
+    assert not bad.any(), summary(got, ref)
+    tail = buf[pad + M * N:].float().cpu().numpy()
+    assert np.isnan(tail).all(), "C written past its last element"
+    if pad:
+        assert np.isnan(buf[:pad].float().cpu().numpy()).all(), "C written before its first element"
