@@ -61,15 +61,19 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, sha: str):
+def load_traffic(workload: str, precision: str, a_format: str, b_format: str, ring: str, sha: str):
     """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"mxgemm_traffic_{workload}.json")
+    they were taken on the current kernel sources for the same GEMM kernel
+    (precision mode, operand formats and ring protocol)."""
+    path = os.path.join(ROOT, "profiles", f"mxgemm_traffic_{workload}_{precision}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
     if d.get("kernel_source_sha") != sha:
+        return None
+    if (d.get("precision"), d.get("a_format"), d.get("b_format"), d.get("ring")) != (
+            precision, a_format, b_format, ring):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -416,7 +420,8 @@ def main():
                 os.remove(f)
 
     sha = kernel_source_sha()
-    traffic = load_traffic(args.config, sha)
+    traffic = load_traffic(args.config, args.precision, args.a_format, args.b_format,
+                           "flags" if plan["ring"] == pkg.RING_FLAGS else "events", sha)
 
     value = flops / (ms_mean * 1e-3) / 1e12
     out = {
