@@ -85,10 +85,14 @@ enum { MXGEMM_FMT_E4M3 = 0, MXGEMM_FMT_E5M2 = 1 };
  *    run, holds its B tile (64 rows x the split's K range, at most 1024) in
  *    LDS, stages its share of every window into the ring, and hands over
  *    through counters in device memory: ready and credit per (slot group,
- *    split), polled with agent-scope acquire and released with agent-scope
- *    release.  The last split to finish a tile sums the FP32 partials in
- *    split order.  One launch and one read of B instead of one per window:
- *    for short M (skinny shapes).  Both precision modes.  All work-groups
+ *    split).  Everything one work-group writes for another (ring data,
+ *    partials, counters) goes through device-scope stores and loads, and a
+ *    count is raised only after the writer's stores have completed.  The
+ *    last split to finish a tile sums the FP32 partials in split order.
+ *    One launch and one read of B instead of one per window, for short M
+ *    (skinny shapes); chosen only when asked for (options.ring), since the
+ *    device-memory hand-overs made it slower than the events protocol on
+ *    every measured shape.  Both precision modes.  All work-groups
  *    must be resident at once (at most one per compute unit); a wait that
  *    polls spin_limit times without progress gives up, marks the handle
  *    (mxgemm_seg_status) and lets the kernel finish, so a run never hangs.
@@ -132,7 +136,7 @@ typedef struct mxgemm_seg_options {
     int32_t precision;         /* MXGEMM_PRECISION_* (-1 = EXACT)           */
     int32_t a_format;          /* MXGEMM_FMT_* of A (-1 = E4M3)             */
     int32_t b_format;          /* MXGEMM_FMT_* of B (-1 = E4M3)             */
-    int32_t ring;              /* MXGEMM_RING_* (-1 = planner's choice)     */
+    int32_t ring;              /* MXGEMM_RING_* (-1 = EVENTS)               */
     int32_t spin_limit;        /* flags protocol: polls per wait (-1 = ~1 s) */
 } mxgemm_seg_options_t;
 

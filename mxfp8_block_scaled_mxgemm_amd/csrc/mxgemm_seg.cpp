@@ -107,8 +107,11 @@ double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int s
     if (split > 1) {
         if (fused_combine(t.tile_m, t.tile_n, split)) {
             // the last split of each tile reads the tile's partials (~12
-            // B/clock per CU) after a device-scope round trip
-            total += (double)t.tile_m * t.tile_n * split * 4.0 / 12.0 + 3000.0;
+            // B/clock per CU) after a chain of device-memory round trips
+            // (partial stores complete, arrival count, partial loads): ~9000
+            // clocks, from runs of one shape with and without the split
+            // (128 x 256 x 512, 16 x 64 tiles: 13.3 vs 11.8 us per run)
+            total += (double)t.tile_m * t.tile_n * split * 4.0 / 12.0 + 9000.0;
         } else {
             // FP32 partials written and read back, C written, by a second
             // launch: bytes at ~2.5 TB/s (measured), plus the launch
@@ -135,19 +138,6 @@ int ring_split(int64_t kpr, int32_t R, int64_t N, int num_cus)
             best = s;
     }
     return best;
-}
-
-// Estimated time of a flags-protocol run, in 2.4 GHz clocks: launch and
-// first hand-over, one hand-over per further window, the bytes one
-// work-group copies at the per-CU copy rate (~12 B/clock), and the MFMA and
-// conversion work of its tile rows.
-double estimate_ring(int64_t M, int64_t kpr, int32_t R, int s, int windows, int tiles_m_win)
-{
-    const double kr = (double)(R / s) * kpr * 33.0 / 32.0;
-    const double bytes = kr * (mxg::kRingBN + (double)M);
-    const double steps = (double)(R / s) * (kpr / 128);
-    return 12000.0 + 5000.0 * (windows - 1) + bytes / 12.0 +
-           (double)windows * tiles_m_win * steps * 350.0;
 }
 
 constexpr int kDefaultSpinLimit = 1 << 19;
@@ -226,6 +216,13 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
                     continue;
                 if (c == mxg::kOneShotCfg && (int64_t)(R / s) * (kpr / 128) > mxg::kOneShotSteps)
                     continue;   // a work item's K range must fit the single stage
+                // The one-shot tile only when asked for: measured against the
+                // pipelined 16 x 64 tile (two work-groups per CU) it was
+                // slower on every shape it fits (64 x 2048 x 7168: 37.4 vs
+                // 33.9 us per run; 128 x 256 x 512: 12.2 vs 11.8 us), which
+                // this cost model does not predict.
+                if (c == mxg::kOneShotCfg && !(opts && opts->tile_cfg == c))
+                    continue;
                 const double gemm = estimate(mxg::tile_cfg(c), rows, N, p->K, s, num_cus, exact);
                 const double cost = overlap
                     ? (double)windows * (gemm > stage ? gemm : stage) + stage
@@ -277,12 +274,14 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     p->ring = MXGEMM_RING_EVENTS;
     p->spin_limit = opts && opts->spin_limit >= 0 ? opts->spin_limit : kDefaultSpinLimit;
 
-    // Flags protocol: when the options allow it and it is estimated faster
-    // (or it is asked for)
+    // Flags protocol: only when asked for.  Measured against the events
+    // protocol it was slower on every shape it fits (64 x 2048 x 7168: 71.8
+    // vs 36.7 us per run, stream-issued), its windows being chains of
+    // device-memory round trips.
     const int want = opts ? opts->ring : -1;
     if (want != -1 && want != MXGEMM_RING_EVENTS && want != MXGEMM_RING_FLAGS)
         return fail(MXGEMM_EINVAL, "unknown ring protocol %d", want);
-    if (want == MXGEMM_RING_EVENTS)
+    if (want != MXGEMM_RING_FLAGS)
         return MXGEMM_OK;
     const bool forced_tiles = opts && (opts->tile_cfg >= 0 || opts->split > 0);
     int s = !forced_tiles ? ring_split(kpr, R, N, num_cus) : 0;
@@ -298,16 +297,10 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
         if (words > (1 << 20) || ws > (1LL << 32))
             s = 0;
     }
-    if (s == 0) {
-        if (want == MXGEMM_RING_FLAGS)
-            return fail(MXGEMM_EUNSUPPORTED, "the flags protocol needs no forced tile or split, a "
-                        "split whose K range is at most %d K-steps of 128 and at most one "
-                        "work-group per compute unit (%d)", mxg::kRingMaxSteps, num_cus);
-        return MXGEMM_OK;
-    }
-    const double ring_cost = estimate_ring(M, kpr, R, s, (int)windows_r, (int)tiles_m_win);
-    if (want != MXGEMM_RING_FLAGS && ring_cost >= best.cost)
-        return MXGEMM_OK;
+    if (s == 0)
+        return fail(MXGEMM_EUNSUPPORTED, "the flags protocol needs no forced tile or split, a "
+                    "split whose K range is at most %d K-steps of 128 and at most one "
+                    "work-group per compute unit (%d)", mxg::kRingMaxSteps, num_cus);
     p->ring = MXGEMM_RING_FLAGS;
     p->chunks_per_window = Wr;
     p->windows = (int32_t)windows_r;

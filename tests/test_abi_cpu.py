@@ -200,3 +200,17 @@ def test_one_shot_tile_needs_short_k_range():
     # the planner never picks it where it does not fit
     p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(split=1))
     assert p.tile_cfg != 6
+
+
+def test_automatic_plan_is_events_without_one_shot_tile():
+    """Without options the planner uses the events protocol and never the
+    one-shot tile (both only on request); forcing either still works."""
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    from mxfp8_block_scaled_mxgemm_amd import inputs
+    for w in inputs.WORKLOADS.values():
+        p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
+        assert p.ring == pkg.RING_EVENTS and p.tile_cfg != 6, w.describe()
+    p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(tile_cfg=6))
+    assert p.tile_cfg == 6 and p.ring == pkg.RING_EVENTS
+    p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(ring="flags"))
+    assert p.ring == pkg.RING_FLAGS
