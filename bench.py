@@ -61,10 +61,12 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(workload: str, precision: str, a_format: str, b_format: str, ring: str, sha: str):
+def load_traffic(workload: str, precision: str, a_format: str, b_format: str, ring: str, plan: dict,
+                 sha: str):
     """HBM bytes per GEMM launch from committed rocprofv3 counter runs, if
-    they were taken on the current kernel sources for the same GEMM kernel
-    (precision mode, operand formats and ring protocol)."""
+    they were taken on the current kernel sources for the same GEMM launch
+    (precision mode, operand formats, ring protocol, tile configuration,
+    split and window)."""
     path = os.path.join(ROOT, "profiles", f"mxgemm_traffic_{workload}_{precision}.json")
     if not os.path.exists(path):
         return None
@@ -74,6 +76,8 @@ def load_traffic(workload: str, precision: str, a_format: str, b_format: str, ri
         return None
     if (d.get("precision"), d.get("a_format"), d.get("b_format"), d.get("ring")) != (
             precision, a_format, b_format, ring):
+        return None
+    if d.get("plan") != {k: plan[k] for k in ("tile_cfg", "split", "chunks_per_window")}:
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -421,7 +425,7 @@ def main():
 
     sha = kernel_source_sha()
     traffic = load_traffic(args.config, args.precision, args.a_format, args.b_format,
-                           "flags" if plan["ring"] == pkg.RING_FLAGS else "events", sha)
+                           "flags" if plan["ring"] == pkg.RING_FLAGS else "events", plan, sha)
 
     value = flops / (ms_mean * 1e-3) / 1e12
     out = {
