@@ -439,7 +439,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",
+        # the arithmetic the GEMM runs in: exact mode widens the FP8 codes
+        # (scale folded in, exactly) to bfloat16 for the bf16 MFMA with FP32
+        # accumulation; native mode multiplies the FP8 codes on the scaled
+        # FP8 MFMA.  Inputs are MXFP8 either way.
+        "dtype": "bf16" if args.precision == "exact" else "fp8",
+        "inputs_dtype": f"mx{args.a_format}/mx{args.b_format} (E8M0 per 32), bf16 out",
         "data": "synthetic",
         "config": {"workload": f"{args.config}: {w.describe()}, "
                                f"N(0,{w.sigma:g})" + (f" with {w.outlier_frac:.0%} of entries "
