@@ -1,0 +1,51 @@
+"""Host logic of bench.py: the HBM-traffic figures it reports come only from
+counter runs of the same GEMM launch on the same kernel sources."""
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+PLAN = {"tile_cfg": 0, "split": 1, "chunks_per_window": 4, "ring": 0, "windows": 4}
+
+
+def _write(tmp_path, monkeypatch, **over):
+    d = {"kernel_source_sha": "abc", "workload": "w", "precision": "exact", "a_format": "e4m3",
+         "b_format": "e4m3", "ring": "events", "plan": {"tile_cfg": 0, "split": 1, "chunks_per_window": 4},
+         "hbm_bytes_per_launch": 123}
+    d.update(over)
+    os.makedirs(tmp_path / "profiles", exist_ok=True)
+    with open(tmp_path / "profiles" / "mxgemm_traffic_w_exact.json", "w") as f:
+        json.dump(d, f)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+
+
+def test_traffic_matches_only_the_same_launch(tmp_path, monkeypatch):
+    _write(tmp_path, monkeypatch)
+    assert bench.load_traffic("w", "exact", "e4m3", "e4m3", "events", PLAN, "abc") == 123
+    assert bench.load_traffic("w", "exact", "e4m3", "e4m3", "events", PLAN, "other") is None
+    assert bench.load_traffic("w", "native", "e4m3", "e4m3", "events", PLAN, "abc") is None
+    assert bench.load_traffic("w", "exact", "e5m2", "e4m3", "events", PLAN, "abc") is None
+    assert bench.load_traffic("w", "exact", "e4m3", "e4m3", "flags", PLAN, "abc") is None
+    assert bench.load_traffic("w", "exact", "e4m3", "e4m3", "events", dict(PLAN, split=2), "abc") is None
+    assert bench.load_traffic("x", "exact", "e4m3", "e4m3", "events", PLAN, "abc") is None
+
+
+def test_traffic_files_in_tree_name_their_launch():
+    """Every committed traffic file records the kernel sources, mode,
+    formats, ring and plan it was counted on, and the summary it came from."""
+    prof = os.path.join(ROOT, "profiles")
+    files = [f for f in os.listdir(prof) if f.startswith("mxgemm_traffic_")]
+    assert files
+    for name in files:
+        with open(os.path.join(prof, name)) as f:
+            d = json.load(f)
+        for key in ("kernel_source_sha", "precision", "a_format", "b_format", "ring", "plan",
+                    "hbm_bytes_per_launch", "source"):
+            assert key in d, (name, key)
+        assert name == f"mxgemm_traffic_{d['workload']}_{d['precision']}.json"
+        assert os.path.exists(os.path.join(ROOT, d["source"]))
