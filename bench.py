@@ -489,6 +489,14 @@ def main():
             "stage_us_per_launch": round(stage_ms_per_launch * 1e3, 3),
         },
         "kernel_source_sha": sha,
+        # what "correct" means for this output (checked by the GPU tests
+        # against the CPU oracle, not by the timed run)
+        "acceptance": {
+            "tolerance": "|gpu - oracle| <= 1e-2 + 8e-3 |oracle| elementwise, NaN fails; "
+                         "quantiser codes and scales bit-exact",
+            "pages_threshold": "the source's own check is allclose with rtol = atol = 1e-2 "
+                               "on the bfloat16 output (context)",
+        },
     }
     g.close()
     del flush, a_q, a_s, b_q, b_s, c
