@@ -11,7 +11,8 @@ all_to_all_matmul.cpp, argument parsing and host buffer sizing): every one of
 ``R * kPerRank``; B is held transposed as ``[N, K]`` (the kernel entry sets
 TransB, all_to_all_matmul_impl.h, kernel entries).
 
-The five workloads below are the sizes this library is measured on.  Each is
+The five workloads below are the sizes this library is measured on; a
+sixth is the source's own example shape.  Each is
 drawn from ``numpy.random.default_rng(seed)`` (PCG64) as fp32 normals; the
 outlier workload then multiplies an independent 1 % of A's entries, and then
 of B's, by 100.
@@ -65,6 +66,9 @@ WORKLOADS: Dict[str, Workload] = {
     "m4096_n4096_k7168": Workload("m4096_n4096_k7168", 8, 4096, 896, 4096, 512, 4, 0.5, 0.0, 1.0, 103),
     "skinny_m64_n2048_k7168": Workload("skinny_m64_n2048_k7168", 8, 64, 896, 2048, 8, 4, 1.0, 0.0, 1.0, 104),
     "outlier_m8192_n8192_k8192": Workload("outlier_m8192_n8192_k8192", 8, 8192, 1024, 8192, 512, 4, 1.0, 0.01, 100.0, 105),
+    # the performance example of the source's host program (m 2048, k 8192,
+    # n 3584, 4 ranks) with its chunk size 512 and ring depth 4
+    "example_m2048_n3584_k8192": Workload("example_m2048_n3584_k8192", 4, 2048, 2048, 3584, 512, 4, 1.0, 0.0, 1.0, 106),
 }
 
 

@@ -108,7 +108,10 @@ def test_parity_full(name, precision):
     assert not bad.any()
 
 
-@pytest.mark.parametrize("name,precision", [("m4096_n4096_k7168", "exact"), ("m4096_n4096_k7168", "native"), ("outlier_m8192_n8192_k8192", "exact")])
+@pytest.mark.parametrize("name,precision", [("m4096_n4096_k7168", "exact"), ("m4096_n4096_k7168", "native"),
+                                            ("outlier_m8192_n8192_k8192", "exact"),
+                                            ("example_m2048_n3584_k8192", "exact"),
+                                            ("example_m2048_n3584_k8192", "native")])
 def test_parity_sampled(name, precision):
     torch_cuda()
     case = _case(name)
