@@ -128,7 +128,20 @@ typedef struct mxgemm_seg_plan {
     int64_t workspace_bytes;   /* FP32 split-K partials: S * W * commMSize * N * 4 */
 } mxgemm_seg_plan_t;
 
-/* Optional knobs for mxgemm_seg_create_ex / mxgemm_seg_plan; -1 = automatic. */
+/* Optional knobs for mxgemm_seg_create_ex / mxgemm_seg_plan; -1 = automatic.
+ *
+ * Tile table (tile_cfg: work-group tile of C, K-steps of 128 per LDS stage):
+ *   0  256 x 256, 1 step   (exact: 4 waves of 128 x 128; native: 8 waves)
+ *   1  256 x 128, 1 step
+ *   2  128 x 128, 1 step
+ *   3   64 x  64, 2 steps  (two work-groups per compute unit)
+ *   4   32 x  64, 3 steps  (two per compute unit)
+ *   5   16 x  64, 3 steps  (two per compute unit)
+ *   6   32 x  64, one stage holding a work item's whole K range, at most 8
+ *       steps ((rank_size / split) * kPerRank / 128 <= 8); planned only when
+ *       asked for
+ * The planner picks the tile, split and window by a cost model; forcing a
+ * value the problem cannot take fails with MXGEMM_EINVAL. */
 typedef struct mxgemm_seg_options {
     int32_t tile_cfg;          /* force a tile configuration (table index)  */
     int32_t split;             /* force S (must divide rank_size)           */
