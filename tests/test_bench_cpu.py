@@ -49,3 +49,14 @@ def test_traffic_files_in_tree_name_their_launch():
             assert key in d, (name, key)
         assert name == f"mxgemm_traffic_{d['workload']}_{d['precision']}.json"
         assert os.path.exists(os.path.join(ROOT, d["source"]))
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py runs on one GPU: --gpus N > 1 exits with a message before
+    touching a device."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
