@@ -260,6 +260,17 @@ def main():
     c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    # identity of the run's inputs: SHA-256 of the quantised operands as they
+    # sit in device memory (A codes, A scales, B codes, B scales, in order)
+    hq = hashlib.sha256()
+    for t in (a_q, a_s, b_q, b_s):
+        hq.update(t.cpu().numpy().tobytes())
+    inputs_sha = hq.hexdigest()[:16]
+    props = torch.cuda.get_device_properties(dev)
+    import numpy as _np
+    env = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count, "torch": torch.__version__,
+           "hip": torch.version.hip, "numpy": _np.__version__}
 
     opts = None
     prec = pkg.PRECISION_EXACT if args.precision == "exact" else pkg.PRECISION_NATIVE
@@ -489,6 +500,8 @@ def main():
             "stage_us_per_launch": round(stage_ms_per_launch * 1e3, 3),
         },
         "kernel_source_sha": sha,
+        "inputs_sha256": inputs_sha,
+        "env": env,
         # what "correct" means for this output (checked by the GPU tests
         # against the CPU oracle, not by the timed run)
         "acceptance": {

@@ -470,6 +470,9 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
     h->plan = plan;
     h->device = dev;
     auto oom = [&](const char* what, size_t bytes) {
+        // the failed hipMalloc also set the thread's last HIP error; clear
+        // it, or the next launch check (hipGetLastError) would report it
+        (void)hipGetLastError();
         release(h);
         return fail(MXGEMM_ENOMEM, "allocating %s (%zu bytes) failed", what, bytes);
     };

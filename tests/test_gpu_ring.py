@@ -144,3 +144,22 @@ def test_profiling_counts_launches():
         assert t["gemm_ms"] > 0 and t["stage_ms"] > 0
         bad, _ = within_tol(c.float().cpu().numpy(), case.oracle_full())
         assert not bad.any()
+
+
+def test_allocation_failure_is_enomem_and_leaves_no_error_behind():
+    """create() with a split-K workspace far beyond device memory (8 splits
+    x 65536 rows x 2^20 columns x 4 bytes = 2 TiB) fails with ENOMEM, frees
+    what it had allocated, and leaves no HIP error that a later handle's
+    launch checks would pick up."""
+    torch = torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    from mxfp8_block_scaled_mxgemm_amd import _lib
+    say("[enomem] 2 TiB workspace request")
+    with pytest.raises(pkg.MxgemmError) as ei:
+        pkg.SegGemm(65536, 128, 8, 1 << 20, 65536, 1, opts=pkg.options(tile_cfg=0, split=8))
+    assert ei.value.code == _lib.MXGEMM_ENOMEM
+    case = _case()
+    got = case.run_gpu().float().cpu().numpy()
+    torch.cuda.synchronize()
+    bad, _ = within_tol(got, case.oracle_full())
+    assert not bad.any()
