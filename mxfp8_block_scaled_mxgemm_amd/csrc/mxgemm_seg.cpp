@@ -30,11 +30,16 @@ int fail(int code, const char* fmt, ...)
     return code;
 }
 
+// A failing HIP call is reported through the return code and the message;
+// the thread's last HIP error is cleared so that a later, unrelated launch
+// check does not report it again.
 #define HIP_TRY(expr)                                                                   \
     do {                                                                                \
         hipError_t e_ = (expr);                                                         \
-        if (e_ != hipSuccess)                                                           \
+        if (e_ != hipSuccess) {                                                         \
+            (void)hipGetLastError();                                                    \
             return fail(MXGEMM_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));    \
+        }                                                                               \
     } while (0)
 
 bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -490,6 +495,7 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
         if (hipMalloc((void**)&h->tile_cnt, bytes) != hipSuccess)
             return oom("split-K tile counters", bytes);
         if (hipMemset(h->tile_cnt, 0, bytes) != hipSuccess) {
+            (void)hipGetLastError();
             release(h);
             return fail(MXGEMM_EHIP, "clearing the split-K tile counters failed");
         }
@@ -502,6 +508,7 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
         if (hipMalloc((void**)&h->sync, bytes) != hipSuccess)
             return oom("ring counters", bytes);
         if (hipMemset(h->sync, 0, bytes) != hipSuccess) {
+            (void)hipGetLastError();
             release(h);
             return fail(MXGEMM_EHIP, "clearing the ring counters failed");
         }
@@ -519,6 +526,7 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
     if (e == hipSuccess)
         e = hipDeviceSynchronize();
     if (e != hipSuccess) {
+        (void)hipGetLastError();
         release(h);
         return fail(MXGEMM_EHIP, "handle setup failed: %s", hipGetErrorString(e));
     }
