@@ -265,6 +265,8 @@ def quantize_mxfp8(x, q=None, s=None, stream=None, fmt=FMT_E4M3):
     uint8 scales [rows, cols/32]).  Outputs may be given (views with unit
     last stride)."""
     import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError("x must be a device tensor")
     if x.dtype != torch.float32 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D float32 tensor with contiguous rows")
     rows, cols = x.shape
@@ -272,6 +274,9 @@ def quantize_mxfp8(x, q=None, s=None, stream=None, fmt=FMT_E4M3):
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    for t in (q, s):
+        if not isinstance(t, torch.Tensor) or t.device != x.device or t.dtype != torch.uint8:
+            raise TypeError("outputs must be uint8 tensors on x's device")
     if q.stride(1) != 1 or s.stride(1) != 1 or tuple(q.shape) != (rows, cols) \
             or tuple(s.shape) != (rows, cols // 32):
         raise ValueError("bad output tensors")

@@ -214,3 +214,17 @@ def test_automatic_plan_is_events_without_one_shot_tile():
     assert p.tile_cfg == 6 and p.ring == pkg.RING_EVENTS
     p = pkg.plan(64, 896, 8, 2048, 8, 4, opts=pkg.options(ring="flags"))
     assert p.ring == pkg.RING_FLAGS
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes raw pointers to GPU kernels: tensors in host memory
+    are refused before any call reaches the library."""
+    import torch
+    x = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(TypeError):
+        pkg.quantize_mxfp8(x)
+    with pytest.raises(TypeError):
+        pkg.quantize_segments(torch.zeros((4, 128), dtype=torch.float32), 2)
+    from mxfp8_block_scaled_mxgemm_amd import _lib
+    with pytest.raises(TypeError):
+        _lib._dptr(x)
