@@ -214,7 +214,11 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
  * after run() on `stream` therefore stays
  * ordered and the call can be captured into a HIP graph.  A handle must not
  * be run concurrently on two streams; distinct handles may.
- * Errors: EINVAL (NULL handle/pointer, misaligned pointer), EHIP.
+ * Errors: EINVAL (NULL handle/pointer, misaligned pointer; a buffer the
+ * GPU cannot access, i.e. host memory that is not pinned, or device memory
+ * of another device), EHIP.  The accessibility check runs when the pointers
+ * differ from the last ones that passed, and enqueues nothing.  Buffer
+ * sizes are not checked: each buffer must hold the bytes stated above.
  */
 int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const void* b,
                    const void* b_scale, void* c, void* stream);

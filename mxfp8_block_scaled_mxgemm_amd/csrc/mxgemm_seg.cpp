@@ -328,6 +328,7 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
 struct mxgemm_seg {
     mxgemm_seg_plan_t plan;
     int device;
+    const void* checked[5];   // run() buffers last found accessible and large enough
     uint8_t* ring;
     uint8_t* sring;
     float* ws;
@@ -373,6 +374,43 @@ void release(mxgemm_seg* h)
     if (h->tile_cnt)
         (void)hipFree(h->tile_cnt);
     delete h;
+}
+
+// The run() buffers must be memory the GPU can read: device memory of the
+// handle's device, managed memory or pinned host memory.  Pageable host
+// memory would fault the kernels, so it is refused before anything is
+// enqueued.  Checked whenever the pointers differ from the last ones that
+// passed (so a steady loop, and graph capture after an eager run, make no
+// extra calls).  Buffer sizes are the caller's contract and are not
+// checked: an allocation's range as the runtime reports it need not be all
+// of the memory mapped behind a pointer.
+int check_buffers(mxgemm_seg* h, const void* const (&ptr)[5])
+{
+    static const char* const names[5] = {"a_seg", "a_scale", "b", "b_scale", "c"};
+    bool same = true;
+    for (int i = 0; i < 5; ++i)
+        same = same && ptr[i] == h->checked[i];
+    if (same)
+        return MXGEMM_OK;
+    for (int i = 0; i < 5; ++i) {
+        hipPointerAttribute_t at;
+        hipError_t e = hipPointerGetAttributes(&at, ptr[i]);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(MXGEMM_EINVAL, "%s: no pointer attributes (%s)", names[i], hipGetErrorString(e));
+        }
+        if (at.type == hipMemoryTypeDevice) {
+            if (at.device != h->device)
+                return fail(MXGEMM_EINVAL, "%s is memory of device %d, the handle's device is %d",
+                            names[i], at.device, h->device);
+        } else if (at.type != hipMemoryTypeManaged && at.type != hipMemoryTypeHost) {
+            return fail(MXGEMM_EINVAL, "%s is not memory the GPU can access (host memory that is "
+                        "not pinned?)", names[i]);
+        }
+    }
+    for (int i = 0; i < 5; ++i)
+        h->checked[i] = ptr[i];
+    return MXGEMM_OK;
 }
 
 int harvest(mxgemm_seg* h)
@@ -563,6 +601,12 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         return fail(MXGEMM_EINVAL, "c must be 2-byte aligned");
     const mxgemm_seg_plan_t& P = h->plan;
     hipStream_t st = (hipStream_t)stream;
+    {
+        const void* const ptr[5] = {a_seg, a_scale, b, b_scale, c};
+        int rc = check_buffers(h, ptr);
+        if (rc != MXGEMM_OK)
+            return rc;
+    }
 
     if (h->profiling) {
         int rc = harvest(h);

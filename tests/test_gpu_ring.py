@@ -163,3 +163,35 @@ def test_allocation_failure_is_enomem_and_leaves_no_error_behind():
     torch.cuda.synchronize()
     bad, _ = within_tol(got, case.oracle_full())
     assert not bad.any()
+
+
+def test_run_refuses_host_memory_the_gpu_cannot_use():
+    """run() checks its buffers before enqueuing anything: pageable host
+    memory in any argument is refused with EINVAL, and a correct call right
+    after still runs."""
+    torch = torch_cuda()
+    import mxfp8_block_scaled_mxgemm_amd as pkg
+    from mxfp8_block_scaled_mxgemm_amd import _lib
+    case = _case()
+    w = case.w
+    c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    host = np.zeros(w.M * w.N * 2 + 64, dtype=np.uint8)         # pageable host memory
+    host_ptr = (host.ctypes.data + 15) // 16 * 16
+    lib = _lib.load()
+    ptrs = [case.a_q.data_ptr(), case.a_s.data_ptr(), case.b_q.data_ptr(), case.b_s.data_ptr(),
+            c.data_ptr()]
+    with pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf) as g:
+        for i in range(5):
+            bad = list(ptrs)
+            bad[i] = host_ptr
+            say(f"[buffers] host pointer in argument {i}")
+            rc = lib.mxgemm_seg_run(g._h, *[ctypes.c_void_p(x) for x in bad], None)
+            assert rc == _lib.MXGEMM_EINVAL, lib.mxgemm_seg_last_error()
+            assert b"not memory the GPU can access" in lib.mxgemm_seg_last_error()
+        torch.cuda.synchronize()
+        c.fill_(float("nan"))
+        g.run(case.a_q, case.a_s, case.b_q, case.b_s, c)
+        torch.cuda.synchronize()
+    got = c.float().cpu().numpy()
+    bad, _ = within_tol(got, case.oracle_full())
+    assert not bad.any()
