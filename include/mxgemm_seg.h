@@ -281,7 +281,8 @@ int mxgemm_quantize_mxfp8(const float* x, int64_t rows, int64_t cols, int64_t ld
  * the rule uses its largest finite value: e = the smallest integer with
  * 57344 * 2^e >= amax, clamped to [-127, 127], and codes are E5M2
  * round-to-nearest-even of x * 2^-e, saturating at 57344 (MX conversions
- * saturate).  Errors: EINVAL (also for an unknown format), EHIP.
+ * saturate).  Errors: EINVAL (also for an unknown format, and for x, q or
+ * s in memory the GPU cannot access, such as pageable host memory), EHIP.
  */
 int mxgemm_quantize_mx(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
                        uint8_t* q, int64_t ld_q, uint8_t* s, int64_t ld_s, int32_t format,

@@ -384,6 +384,26 @@ void release(mxgemm_seg* h)
 // extra calls).  Buffer sizes are the caller's contract and are not
 // checked: an allocation's range as the runtime reports it need not be all
 // of the memory mapped behind a pointer.
+int gpu_accessible(const void* p, const char* name, int device)
+{
+    hipPointerAttribute_t at;
+    hipError_t e = hipPointerGetAttributes(&at, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MXGEMM_EINVAL, "%s: no pointer attributes (%s)", name, hipGetErrorString(e));
+    }
+    if (at.type == hipMemoryTypeDevice) {
+        if (at.device != device)
+            return fail(MXGEMM_EINVAL, "%s is memory of device %d, not of device %d", name, at.device,
+                        device);
+        return MXGEMM_OK;
+    }
+    if (at.type == hipMemoryTypeManaged || at.type == hipMemoryTypeHost)
+        return MXGEMM_OK;
+    return fail(MXGEMM_EINVAL, "%s is not memory the GPU can access (host memory that is not "
+                "pinned?)", name);
+}
+
 int check_buffers(mxgemm_seg* h, const void* const (&ptr)[5])
 {
     static const char* const names[5] = {"a_seg", "a_scale", "b", "b_scale", "c"};
@@ -393,20 +413,9 @@ int check_buffers(mxgemm_seg* h, const void* const (&ptr)[5])
     if (same)
         return MXGEMM_OK;
     for (int i = 0; i < 5; ++i) {
-        hipPointerAttribute_t at;
-        hipError_t e = hipPointerGetAttributes(&at, ptr[i]);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return fail(MXGEMM_EINVAL, "%s: no pointer attributes (%s)", names[i], hipGetErrorString(e));
-        }
-        if (at.type == hipMemoryTypeDevice) {
-            if (at.device != h->device)
-                return fail(MXGEMM_EINVAL, "%s is memory of device %d, the handle's device is %d",
-                            names[i], at.device, h->device);
-        } else if (at.type != hipMemoryTypeManaged && at.type != hipMemoryTypeHost) {
-            return fail(MXGEMM_EINVAL, "%s is not memory the GPU can access (host memory that is "
-                        "not pinned?)", names[i]);
-        }
+        int rc = gpu_accessible(ptr[i], names[i], h->device);
+        if (rc != MXGEMM_OK)
+            return rc;
     }
     for (int i = 0; i < 5; ++i)
         h->checked[i] = ptr[i];
@@ -852,6 +861,17 @@ int mxgemm_quantize_mx(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
     if (ld_x % 4 != 0 || ld_q % 4 != 0 || ((uintptr_t)x & 15u) || ((uintptr_t)q & 3u))
         return fail(MXGEMM_EINVAL, "x must be 16-byte aligned with ld_x % 4 == 0; q 4-byte "
                     "aligned with ld_q % 4 == 0");
+    if (rows > 0 && cols > 0) {
+        int dev = 0;
+        HIP_TRY(hipGetDevice(&dev));
+        int rc = gpu_accessible(x, "x", dev);
+        if (rc == MXGEMM_OK)
+            rc = gpu_accessible(q, "q", dev);
+        if (rc == MXGEMM_OK)
+            rc = gpu_accessible(s, "s", dev);
+        if (rc != MXGEMM_OK)
+            return rc;
+    }
     mxg::QuantArgs a;
     a.x = x;
     a.q = q;

@@ -195,3 +195,31 @@ def test_run_refuses_host_memory_the_gpu_cannot_use():
     got = c.float().cpu().numpy()
     bad, _ = within_tol(got, case.oracle_full())
     assert not bad.any()
+
+
+def test_quantizer_refuses_host_memory():
+    """The quantiser's C entry refuses pageable host memory for its input
+    and outputs before launching, and works on device memory right after."""
+    torch = torch_cuda()
+    from mxfp8_block_scaled_mxgemm_amd import _lib
+    lib = _lib.load()
+    rows, cols = 8, 64
+    x = torch.randn((rows, cols), device="cuda")
+    q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
+    host = np.zeros(rows * cols * 4 + 64, dtype=np.uint8)
+    hp = (host.ctypes.data + 15) // 16 * 16
+    dev = [x.data_ptr(), q.data_ptr(), s.data_ptr()]
+    for i in range(3):
+        args = list(dev)
+        args[i] = hp
+        say(f"[quantiser] host pointer in argument {i}")
+        rc = lib.mxgemm_quantize_mx(ctypes.c_void_p(args[0]), rows, cols, cols, ctypes.c_void_p(args[1]),
+                                    cols, ctypes.c_void_p(args[2]), cols // 32, 0, None)
+        assert rc == _lib.MXGEMM_EINVAL
+        assert b"not memory the GPU can access" in lib.mxgemm_seg_last_error()
+    rc = lib.mxgemm_quantize_mx(ctypes.c_void_p(dev[0]), rows, cols, cols, ctypes.c_void_p(dev[1]), cols,
+                                ctypes.c_void_p(dev[2]), cols // 32, 0, None)
+    assert rc == _lib.MXGEMM_OK
+    torch.cuda.synchronize()
+    assert int(s.max()) > 0
