@@ -56,7 +56,6 @@ def _load():
         lib.oracle_e8m0_exponent.argtypes = [ctypes.c_double]
         lib.oracle_bf16_from_double.restype = ctypes.c_uint16
         lib.oracle_bf16_from_double.argtypes = [ctypes.c_double]
-        lib.oracle_quantize_mxfp8.argtypes = [_f32p, _i64, _i64, _u8p, _u8p]
         lib.oracle_quantize_mx.argtypes = [_f32p, _i64, _i64, _u8p, _u8p, ctypes.c_int]
         lib.oracle_mxgemm_seg.argtypes = [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _i64, _u16p,
                                           ctypes.c_int, ctypes.c_int]

@@ -36,6 +36,15 @@
  *    448 * 2^e >= amax (that is 2^ceil(log2(amax/448))), clamped to
  *    [-127, 127], amax = 0 giving -127; the scale byte is e + 127 and each
  *    element is encoded as e4m3_rne(x * 2^-e), keeping the sign of zero.
+ *  - Non-finite inputs.  A block holding a NaN has no exponent: its scale
+ *    is the E8M0 NaN byte 0xFF and every code of the block is the NaN code
+ *    0x7F (x divided by a NaN scale is NaN).  A block holding an infinity
+ *    (and no NaN) has amax = +inf, for which no integer e satisfies the
+ *    rule; the clamp gives e = 127 (byte 0xFE), infinities encode as the
+ *    largest finite code of their sign (E4M3 has no infinity; the encoder
+ *    saturates) and the finite elements encode as usual.
+ *  - An E8M0 scale byte 0xFF in a GEMM input is NaN, so every output whose
+ *    sum takes a product from that block is NaN.
  *
  * The other FP8 operand formats (all_to_all_matmul_impl.h, the sibling
  * kernel entries E5M2E5M2, E4M3E5M2 and E5M2E4M3): either operand may be
@@ -72,7 +81,8 @@ double oracle_e4m3_value(uint8_t code)
 }
 
 /* E4M3FN code of v, round-to-nearest-even.  Magnitudes above 448 after
- * rounding saturate to 448 (the quantiser below never produces them). */
+ * rounding, infinities included, saturate to 448 (the quantiser produces
+ * them only from infinite inputs); NaN gives 0x7F. */
 uint8_t oracle_e4m3_encode(double v)
 {
     uint8_t sign;
@@ -81,6 +91,8 @@ uint8_t oracle_e4m3_encode(double v)
         return 0x7F;
     sign = signbit(v) ? 0x80 : 0x00;
     a = fabs(v);
+    if (isinf(a))
+        return (uint8_t)(sign | 0x7E);
     if (a < ldexp(1.0, -6)) {
         /* subnormal range: multiples of 2^-9; q == 8 is the smallest
          * normal, whose code is also 8 */
@@ -161,11 +173,17 @@ double oracle_fp8_value(uint8_t code, int fmt)
 
 /* --------------------------------------------------------------- E8M0 --- */
 
-/* Smallest integer e with 448 * 2^e >= amax, clamped to [-127, 127]. */
+/* Smallest integer e with 448 * 2^e >= amax, clamped to [-127, 127]
+ * (amax = 0 gives -127, amax = +inf the clamp 127).  A NaN amax has no such
+ * e and gives 128, whose scale byte e + 127 is the E8M0 NaN 0xFF. */
 int oracle_e8m0_exponent(double amax)
 {
     int E, e;
     double f;
+    if (isnan(amax))
+        return 128;
+    if (isinf(amax))
+        return 127;
     if (!(amax > 0.0))
         return -127;
     f = frexp(amax, &E);                 /* amax = f * 2^E, f in [0.5, 1) */
@@ -179,11 +197,15 @@ int oracle_e8m0_exponent(double amax)
 }
 
 /* Smallest integer e with 57344 * 2^e >= amax (the E5M2 largest finite),
- * clamped to [-127, 127]. */
+ * clamped to [-127, 127]; non-finite amax as oracle_e8m0_exponent. */
 int oracle_e8m0_exponent_e5m2(double amax)
 {
     int E, e;
     double f;
+    if (isnan(amax))
+        return 128;
+    if (isinf(amax))
+        return 127;
     if (!(amax > 0.0))
         return -127;
     f = frexp(amax, &E);
@@ -207,11 +229,20 @@ void oracle_quantize_mx(const float* x, int64_t rows, int64_t cols,
         for (int64_t b = 0; b < nb; ++b) {
             const float* blk = x + i * cols + b * 32;
             double amax = 0.0;
-            int e, j;
+            int e, j, has_nan = 0;
             for (j = 0; j < 32; ++j) {
                 double a = fabs((double)blk[j]);
-                if (a > amax)
+                if (isnan(a))
+                    has_nan = 1;
+                else if (a > amax)
                     amax = a;
+            }
+            if (has_nan) {
+                /* no exponent: NaN scale, every element NaN */
+                s[i * nb + b] = 0xFF;
+                for (j = 0; j < 32; ++j)
+                    q[i * cols + b * 32 + j] = 0x7F;
+                continue;
             }
             e = fmt ? oracle_e8m0_exponent_e5m2(amax) : oracle_e8m0_exponent(amax);
             s[i * nb + b] = (uint8_t)(e + 127);
@@ -219,32 +250,6 @@ void oracle_quantize_mx(const float* x, int64_t rows, int64_t cols,
                 double y = ldexp((double)blk[j], -e);
                 q[i * cols + b * 32 + j] = fmt ? oracle_e5m2_encode(y) : oracle_e4m3_encode(y);
             }
-        }
-    }
-}
-
-/* Quantise a row-major [rows][cols] float32 matrix (cols % 32 == 0) into
- * E4M3 codes [rows][cols] and scale bytes [rows][cols/32]. */
-void oracle_quantize_mxfp8(const float* x, int64_t rows, int64_t cols,
-                           uint8_t* q, uint8_t* s)
-{
-    int64_t nb = cols / 32;
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < rows; ++i) {
-        for (int64_t b = 0; b < nb; ++b) {
-            const float* blk = x + i * cols + b * 32;
-            double amax = 0.0;
-            int e, j;
-            for (j = 0; j < 32; ++j) {
-                double a = fabs((double)blk[j]);
-                if (a > amax)
-                    amax = a;
-            }
-            e = oracle_e8m0_exponent(amax);
-            s[i * nb + b] = (uint8_t)(e + 127);
-            for (j = 0; j < 32; ++j)
-                q[i * cols + b * 32 + j] =
-                    oracle_e4m3_encode(ldexp((double)blk[j], -e));
         }
     }
 }
