@@ -49,17 +49,26 @@ enum {
 typedef struct mxgemm_seg* mxgemm_seg_t;
 
 /* Arithmetic of the GEMM core.
- *  MXGEMM_PRECISION_EXACT (default): every E4M3 x E4M3 x 2^(scales) product
+ *  MXGEMM_PRECISION_EXACT (default): every FP8 x FP8 x 2^(scales) product
  *    is formed exactly (codes are converted to bfloat16 with the block scale
- *    folded in, which is exact) and summed with FP32-grade accumulation on
- *    v_mfma_f32_16x16x32_bf16.  Meets |C - exact| <= 1e-2 + 8e-3 |exact| on
- *    any finite data whose sums stay in FP32 range.
+ *    folded in, which is exact for scale bytes >= 3 with E4M3 codes, >= 10
+ *    with E5M2) and the products are summed into FP32 accumulators on the
+ *    bfloat16 MFMA: v_mfma_f32_32x32x16_bf16 on the 256 x 256, 256 x 128
+ *    and 128 x 128 tiles, v_mfma_f32_16x16x32_bf16 on the smaller ones.  The
+ *    result is an FP32 sum in a fixed order, rounded once to bfloat16; like
+ *    any FP32 sum it can lose small terms to cancellation of large ones
+ *    (2^30 + 1 - 2^30 gives 0).  Tested: |C - exact| <= 1e-2 + 8e-3 |exact|
+ *    on every output of the five measured workloads (the 8192-cube outlier
+ *    workload on every output whose |C| is under 5% of the RMS plus a
+ *    random sample), and bit-exact results on integer-valued data whose
+ *    sums stay below 2^8.
  *  MXGEMM_PRECISION_NATIVE: the CDNA4 block-scaled FP8 MFMA
- *    (v_mfma_scale_f32_16x16x128_f8f6f4) at twice the peak rate.  Its
- *    internal block dot drops products that are ~2^13 times smaller than
- *    another product of the same group of eight, so data with large in-block
- *    dynamic range (outliers) can miss the tolerance above where C is
- *    small. */
+ *    (v_mfma_scale_f32_32x32x64_f8f6f4 on the large tiles,
+ *    v_mfma_scale_f32_16x16x128_f8f6f4 on the small ones) at twice the peak
+ *    rate.  Its internal block dot drops products that are ~2^13 times
+ *    smaller than another product of the same group of eight, so data with
+ *    large in-block dynamic range (outliers) can miss the tolerance above
+ *    where C is small; it meets it on the four workloads without outliers. */
 enum { MXGEMM_PRECISION_EXACT = 0, MXGEMM_PRECISION_NATIVE = 1 };
 
 /* FP8 formats of the A and B codes.  The pages ship four entries of the
@@ -178,7 +187,11 @@ typedef struct mxgemm_seg_options {
 int mxgemm_seg_create(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
                       int64_t N, int64_t commMSize, int32_t buffer_count);
 
-/* As mxgemm_seg_create, with optional knobs (opts may be NULL). */
+/* As mxgemm_seg_create, with optional knobs (opts may be NULL): the tile,
+ * split and window the source fixes in its tiling data (all_to_all_matmul.cpp,
+ * GetTilingData over headMSize x n x ka; all_to_all_matmul_impl.h,
+ * SetupParams), the operand formats of its four kernel entries, and the
+ * ring protocol (MatmulProcess / AllToAllProcess).  Errors as create. */
 int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
                          int64_t N, int64_t commMSize, int32_t buffer_count,
                          const mxgemm_seg_options_t* opts);
@@ -193,6 +206,8 @@ int mxgemm_seg_create_ex(mxgemm_seg_t* out, int64_t M, int64_t kPerRank, int32_t
  * (FP8 codes in the plan's a_format / b_format, E4M3 by default)
  *   b_scale  uint8 E8M0  [N][K/32]
  *   c        bfloat16    [M][N], fully overwritten
+ * A scale byte 0xFF (the E8M0 NaN) makes every output that takes a product
+ * from its block NaN, in both precision modes.
  * Layouts: all_to_all_comm_udma.h, PutSegmentToRank / PutScaleToRank (source
  * offsets r*M*rowBytes + mOffset*rowBytes), all_to_all_matmul.cpp (host
  * buffer sizes), all_to_all_matmul_impl.h (TransB = true, C offset
@@ -224,27 +239,41 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
                    const void* b_scale, void* c, void* stream);
 
 /*
- * Flags protocol: MXGEMM_ETIMEOUT if a device wait of any run since the
- * last call gave up (the work-groups of a run were not all resident at
+ * Flags protocol (the device-flag hand-over of all_to_all_matmul_impl.h,
+ * MatmulProcess waiting on the flag AllToAllProcess sets after a copy):
+ * MXGEMM_ETIMEOUT if a device wait of any run since the last call gave up (the work-groups of a run were not all resident at
  * once, e.g. another kernel held compute units; C of such a run is
  * undefined), else MXGEMM_OK; clears the mark.  Waits for all work on the
  * device.  Always MXGEMM_OK for the events protocol.
  */
 int mxgemm_seg_status(mxgemm_seg_t h);
 
-/* Wait for the handle's work and free everything create() allocated.
- * NULL is accepted.  Errors: EHIP (resources are still released). */
+/* Wait for the handle's work and free everything create() allocated: the
+ * ring, the workspace and counters, the side stream and the events.  This is
+ * the teardown at the end of the source's host run (all_to_all_matmul.cpp,
+ * runAllToAllMatmul: device buffers freed, then the shared window and the
+ * stream released).  NULL is accepted (nothing to free).  Errors: EHIP if
+ * waiting for the work failed; every resource is still released and the
+ * handle must not be used again. */
 int mxgemm_seg_destroy(mxgemm_seg_t h);
 
-/* Message for the last error on the calling thread ("" if none). */
+/* Message for the last failing call on the calling thread ("" if none);
+ * the string is owned by the library and valid until the thread's next
+ * failing call.  The source reports errors the same two ways: a negative
+ * return (all_to_all_matmul.cpp: parseArguments throws and main returns -1,
+ * runAllToAllMatmul returns -1 when initialisation fails) and a message
+ * (the exception text printed with the usage).  Never fails. */
 const char* mxgemm_seg_last_error(void);
 
-/* Copy the live handle's plan. */
+/* Copy the live handle's plan: the launch geometry the source computes on
+ * the host before its launch (all_to_all_matmul.cpp, GetTilingData and
+ * usedCoreNum as the launch's core count).  Errors: EINVAL (NULL). */
 int mxgemm_seg_get_plan(mxgemm_seg_t h, mxgemm_seg_plan_t* out);
 
 /* Compute the plan create() would choose on a device with `num_cus` compute
  * units, without touching a GPU (same rules and errors as create; opts may
- * be NULL). */
+ * be NULL); the host-side tiling step of all_to_all_matmul.cpp
+ * (GetTilingData) for this library's kernels. */
 int mxgemm_seg_plan(mxgemm_seg_plan_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
                     int64_t N, int64_t commMSize, int32_t buffer_count, int32_t num_cus,
                     const mxgemm_seg_options_t* opts);
@@ -270,14 +299,19 @@ int mxgemm_seg_decode(const mxgemm_seg_plan_t* plan, int64_t rows, int32_t w, in
  * s = e + 127, q = E4M3 round-to-nearest-even of x * 2^-e (sign of zero
  * kept).  The pages produce their MXFP8 inputs offline with a generator they
  * do not show (all_to_all_matmul.cpp header: gen_data.py); this is the rule
- * 2^ceil(log2(amax/448)) written out exactly.  Asynchronous on `stream`.
- * Errors: EINVAL, EHIP.
+ * 2^ceil(log2(amax/448)) written out exactly.  Non-finite input: a block
+ * holding a NaN gets scale byte 0xFF (the E8M0 NaN) and every code 0x7F; a
+ * block holding an infinity (and no NaN) gets e = 127 (the clamp), its
+ * infinities the largest finite code of their sign and its finite elements
+ * the rule above.  Asynchronous on `stream`.  Errors: EINVAL, EHIP.
  */
 int mxgemm_quantize_mxfp8(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
                           uint8_t* q, int64_t ld_q, uint8_t* s, int64_t ld_s, void* stream);
 
 /*
- * As mxgemm_quantize_mxfp8 for codes of `format` (MXGEMM_FMT_*).  For E5M2
+ * As mxgemm_quantize_mxfp8 for codes of `format` (MXGEMM_FMT_*), the input
+ * formats of the source's sibling kernel entries (all_to_all_matmul_impl.h,
+ * ...E5M2E5M2, ...E4M3E5M2, ...E5M2E4M3).  For E5M2
  * the rule uses its largest finite value: e = the smallest integer with
  * 57344 * 2^e >= amax, clamped to [-127, 127], and codes are E5M2
  * round-to-nearest-even of x * 2^-e, saturating at 57344 (MX conversions
@@ -289,7 +323,10 @@ int mxgemm_quantize_mx(const float* x, int64_t rows, int64_t cols, int64_t ld_x,
                        void* stream);
 
 /*
- * Kernel timing for measurement.  While enabled, run() brackets every GEMM
+ * Kernel timing for measurement (the source's perf mode in
+ * all_to_all_matmul.cpp times each kernel launch on its own, after a cache
+ * flush, with a stream synchronisation per round).  While enabled, run()
+ * brackets every GEMM
  * kernel launch (on `stream`; a separate split-K reduce kernel after it is
  * outside the bracket, a fused combine inside) and every staging launch
  * (on the stream it runs on) with timing events; the flags protocol's one
@@ -301,8 +338,6 @@ int mxgemm_seg_set_profiling(mxgemm_seg_t h, int32_t enable);
 int mxgemm_seg_kernel_times(mxgemm_seg_t h, double* gemm_ms, int32_t* gemm_launches,
                             double* stage_ms, int32_t* stage_launches);
 
-/* Library version string. */
-const char* mxgemm_seg_version(void);
 
 #ifdef __cplusplus
 }

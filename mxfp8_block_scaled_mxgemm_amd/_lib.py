@@ -25,7 +25,7 @@ EXPORTED = [
     "mxgemm_seg_create", "mxgemm_seg_create_ex", "mxgemm_seg_run", "mxgemm_seg_destroy",
     "mxgemm_seg_last_error", "mxgemm_seg_get_plan", "mxgemm_seg_plan", "mxgemm_seg_decode",
     "mxgemm_quantize_mxfp8", "mxgemm_quantize_mx", "mxgemm_seg_set_profiling",
-    "mxgemm_seg_kernel_times", "mxgemm_seg_status", "mxgemm_seg_version",
+    "mxgemm_seg_kernel_times", "mxgemm_seg_status",
 ]
 
 
@@ -114,7 +114,6 @@ def load():
     lib.mxgemm_seg_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.mxgemm_seg_destroy.argtypes = [vp]
     lib.mxgemm_seg_last_error.restype = ctypes.c_char_p
-    lib.mxgemm_seg_version.restype = ctypes.c_char_p
     lib.mxgemm_seg_get_plan.argtypes = [vp, ctypes.POINTER(Plan)]
     lib.mxgemm_seg_plan.argtypes = [ctypes.POINTER(Plan), i64, i64, i32, i64, i64, i32, i32,
                                     ctypes.POINTER(Options)]

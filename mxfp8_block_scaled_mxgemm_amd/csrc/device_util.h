@@ -35,12 +35,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-// E8M0 scale byte -> 2^(s - 127) as float, branch-free: v_ldexp_f32 gives
-// 2^-127 (a float32 subnormal) for s = 0; the NaN byte 0xFF comes out as
-// +inf.
+// E8M0 scale byte (the low byte of s) -> 2^(s - 127) as float, branch-free:
+// v_ldexp_f32 gives 2^-127 (a float32 subnormal) for s = 0; the NaN byte
+// 0xFF (which ldexp would turn into +inf) is selected to NaN, so every
+// product of its block, zero codes included, is NaN.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s)
 {
-    return __builtin_amdgcn_ldexpf(0x1p-127f, (int)(s & 0xFFu));
+    const uint32_t b = s & 0xFFu;
+    const float v = __builtin_amdgcn_ldexpf(0x1p-127f, (int)b);
+    return b == 0xFFu ? __builtin_nanf("") : v;
 }
 
 // Two FP8 codes (bytes 2h, 2h + 1 of `src`) of format F -> two bfloat16

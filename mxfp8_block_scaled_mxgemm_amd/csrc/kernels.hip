@@ -154,10 +154,12 @@ hipError_t launch_gemm(int cfg, bool exact, int fa, int fb, const GemmArgs& a, h
 
 // ------------------------------------------------------------- quantiser --
 
-// E4M3 (OCP "FN") code of a float with |y| <= 448, round-to-nearest-even,
-// sign of zero kept.  Normal range: keep 3 mantissa bits and round on the
-// 20 dropped bits; below 2^-6 the grid step is 2^-9, so y * 512 rounded to
-// an integer is the code (8 is the smallest normal, code 0x08).
+// E4M3 (OCP "FN") code of a non-NaN float, round-to-nearest-even, sign of
+// zero kept; magnitudes above 448 after rounding (infinities included)
+// saturate to 448 (code 0x7E).  Normal range: keep 3 mantissa bits and
+// round on the 20 dropped bits; below 2^-6 the grid step is 2^-9, so
+// y * 512 rounded to an integer is the code (8 is the smallest normal,
+// code 0x08).
 __device__ __forceinline__ uint32_t e4m3_rne(float y)
 {
     const uint32_t u = __float_as_uint(y);
@@ -207,7 +209,8 @@ __device__ __forceinline__ uint32_t e5m2_rne(float y)
 // format's largest finite value fmax = 1.75 * 2^EMAX (448: EMAX = 8 for
 // E4M3; 57344: EMAX = 15 for E5M2).  With amax = 1.m * 2^x, e = x - EMAX
 // when 1.m <= 1.75, else x - EMAX + 1.  Zero and float32 subnormals give
-// -127 (the clamp).
+// -127 (the clamp), +inf gives 127 (the clamp of an unbounded e); amax is
+// never NaN here (NaN blocks are handled by the caller).
 template <int EMAX>
 __device__ __forceinline__ int e8m0_exponent(float amax)
 {
@@ -215,6 +218,8 @@ __device__ __forceinline__ int e8m0_exponent(float amax)
     const int ex = (int)(u >> 23);
     if (ex == 0)
         return -127;
+    if (ex == 255)
+        return 127;
     int e = ex - 127 - EMAX + ((u & 0x7FFFFFu) > 0x600000u ? 1 : 0);
     e = e < -127 ? -127 : e;
     return e > 127 ? 127 : e;
@@ -226,7 +231,13 @@ __device__ __forceinline__ uint32_t fp8_rne(float y)
     return F == kE5M2 ? e5m2_rne(y) : e4m3_rne(y);
 }
 
-// Eight threads per 32-element block, four elements each.
+// Eight threads per 32-element block, four elements each.  The block's
+// amax is the largest |x| bit pattern: for non-negative floats the integer
+// order is the numeric order, and every NaN pattern lies above +inf
+// (0x7F800000), so a NaN anywhere in the block is seen (a float max would
+// drop it).  A NaN block has no exponent: scale byte 0xFF (the E8M0 NaN)
+// and every code the NaN code 0x7F.  Infinities (with no NaN) give e = 127
+// and saturate to the largest finite code of their sign.
 template <int F>
 __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs p)
 {
@@ -240,19 +251,28 @@ __global__ void __launch_bounds__(256) quantize_kernel(QuantArgs p)
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (valid)
         v = *reinterpret_cast<const float4*>(p.x + row * p.ld_x + cb * 32 + part * 4);
-    float m = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    m = fmaxf(m, __shfl_xor(m, 1, 8));
-    m = fmaxf(m, __shfl_xor(m, 2, 8));
-    m = fmaxf(m, __shfl_xor(m, 4, 8));
+    const uint32_t am = 0x7FFFFFFFu;
+    uint32_t m = max(max(__float_as_uint(v.x) & am, __float_as_uint(v.y) & am),
+                     max(__float_as_uint(v.z) & am, __float_as_uint(v.w) & am));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1, 8));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2, 8));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 4, 8));
     if (!valid)
         return;
-    const int e = e8m0_exponent<F == kE5M2 ? 15 : 8>(m);
-    const uint32_t code = fp8_rne<F>(ldexpf(v.x, -e)) | (fp8_rne<F>(ldexpf(v.y, -e)) << 8) |
-                          (fp8_rne<F>(ldexpf(v.z, -e)) << 16) |
-                          (fp8_rne<F>(ldexpf(v.w, -e)) << 24);
+    uint32_t code;
+    uint8_t sbyte;
+    if (m > 0x7F800000u) {
+        code = 0x7F7F7F7Fu;
+        sbyte = 0xFF;
+    } else {
+        const int e = e8m0_exponent<F == kE5M2 ? 15 : 8>(__uint_as_float(m));
+        code = fp8_rne<F>(ldexpf(v.x, -e)) | (fp8_rne<F>(ldexpf(v.y, -e)) << 8) |
+               (fp8_rne<F>(ldexpf(v.z, -e)) << 16) | (fp8_rne<F>(ldexpf(v.w, -e)) << 24);
+        sbyte = (uint8_t)(e + 127);
+    }
     *reinterpret_cast<uint32_t*>(p.q + row * p.ld_q + cb * 32 + part * 4) = code;
     if (part == 0)
-        p.s[row * p.ld_s + cb] = (uint8_t)(e + 127);
+        p.s[row * p.ld_s + cb] = sbyte;
 }
 
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream)

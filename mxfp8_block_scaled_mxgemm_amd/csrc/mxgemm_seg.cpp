@@ -466,8 +466,6 @@ extern "C" {
 
 const char* mxgemm_seg_last_error(void) { return g_err.c_str(); }
 
-const char* mxgemm_seg_version(void) { return "mxgemm_seg 0.1 (gfx950)"; }
-
 int mxgemm_seg_plan(mxgemm_seg_plan_t* out, int64_t M, int64_t kPerRank, int32_t rank_size,
                     int64_t N, int64_t commMSize, int32_t buffer_count, int32_t num_cus,
                     const mxgemm_seg_options_t* opts)

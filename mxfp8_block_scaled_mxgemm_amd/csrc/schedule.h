@@ -1,4 +1,5 @@
-// Persistent tile scheduler shared by the GEMM kernel and the host planner.
+// Tile scheduler (flattened work ID, zigzag order, XCD remap) shared by the GEMM
+// kernels and the host planner.
 //
 // One GEMM launch covers one window of staged chunks.  Its work is the set of
 // (tile row, tile column, K-split) triples, flattened into one work ID so
@@ -13,9 +14,10 @@
 // time on neighbouring work-groups.
 //
 // Work-groups are dispatched round-robin over the XCDs (block b runs on XCD
-// b % 8), and each XCD has its own L2.  remap_block() gives the blocks of one
-// XCD a contiguous range of logical IDs, so in every round of the persistent
-// loop each XCD works on one compact patch of tiles.
+// b % 8), and each XCD has its own L2.  The GEMM kernels run one work item
+// per work-group; remap_block() gives the work-groups of one XCD a
+// contiguous range of logical IDs, so the work-groups resident on an XCD at
+// one time work on one compact patch of tiles.
 #pragma once
 
 #include <stdint.h>

@@ -31,9 +31,40 @@ def test_library_exports_every_declared_symbol():
     assert sorted(pkg.EXPORTED) == declared
 
 
-def test_version_and_empty_error():
+def test_empty_error_message_is_a_string():
     lib = pkg.load()
-    assert b"gfx950" in lib.mxgemm_seg_version()
+    assert isinstance(lib.mxgemm_seg_last_error(), bytes)
+
+
+# Files and sections of the pages the header may cite.
+_PAGE_SOURCES = ("all_to_all_matmul.cpp", "all_to_all_matmul_impl.h", "all_to_all_comm_udma.h",
+                 "verify_result.py", "Triton-distributed-Ascend performance guide")
+
+
+def _doc_comments():
+    """Declared function -> the comment block that documents it: the
+    nearest comment above the declaration (functions declared back to back
+    share it)."""
+    text = open(HEADER).read()
+    out = {}
+    pos = 0
+    last_comment = None
+    for m in re.finditer(r"/\*.*?\*/|\b(mxgemm_\w+)\s*\(", text, flags=re.S):
+        if m.group(0).startswith("/*"):
+            last_comment = m.group(0)
+        elif m.group(1) not in out:
+            out[m.group(1)] = last_comment
+        pos = m.end()
+    return out
+
+
+def test_every_declaration_cites_a_page():
+    docs = _doc_comments()
+    assert sorted(docs) == _declared_functions()
+    for name, doc in docs.items():
+        assert doc is not None, name
+        flat = " ".join(re.sub(r"\n\s*\*(?!/)", " ", doc).split())
+        assert any(src in flat for src in _PAGE_SOURCES), name
 
 
 @pytest.mark.parametrize("args,code", [
