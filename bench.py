@@ -12,13 +12,19 @@ steps and --warmup-ms of GPU time.
 
 Prints ONE JSON line (rank 0 / the only rank):
   value      = 2*M*N*K / mean step time (steps issued on the stream), in
-               TFLOP/s; the mean over replays of a HIP graph of the step is
-               reported beside it
+               TFLOP/s, for the headline workload (--config, default the
+               8192-cube outlier workload); the mean over replays of a HIP
+               graph of the step is reported beside it
   roofline   = the GEMM kernel's algorithmic FLOP (or bytes, below the ridge
                point) per launch / its mean launch duration (HIP events
                around each launch, on its stream), against the MI355X dense
-               peak of the MFMA form it runs (or HBM)
-  cpu_baseline = the CPU oracle on a bounded row sample of the same workload
+               MX-FP8 MFMA peak (the metric's peak; the bf16 MFMA peak of the
+               exact mode's contraction beside it) or HBM
+  configs    = the same figures, stream timer only, for the other workloads
+  measured_peaks = an MFMA-rate probe (scaled FP8 and bf16) and a device copy
+               of 1 GiB, the measured denominators beside the published ones
+  cpu_baseline = the CPU oracle on a bounded row sample of the headline
+               workload
 """
 from __future__ import annotations
 
@@ -186,6 +192,92 @@ def cpu_baseline(w, target_s: float):
                       f"on {threads} threads of {cpu}"}
 
 
+def gemm_roofline(w, plan, gemm_ms_per_launch, precision, ring_flags):
+    """Roofline of the GEMM kernel for one workload: achieved FLOP/s (or
+    bytes/s below the ridge point) per launch against the MX-FP8 peak (the
+    metric's; the contraction's own MFMA peak beside it) or HBM."""
+    launches = 1 if ring_flags else plan["windows"]
+    flops_per_launch = float(w.flops) / launches
+    rows_w = w.M / launches
+    # algorithmic bytes of one GEMM launch: A rows and B with their E8M0
+    # scales, C in bfloat16
+    bytes_per_launch = (rows_w * w.K + w.N * w.K) * 33 / 32 + rows_w * w.N * 2
+    kernel_peak = PEAK_BF16_TFLOPS if precision == "exact" else PEAK_FP8_TFLOPS
+    hbm_bound = flops_per_launch / bytes_per_launch < PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    tflops = flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
+    gbs = bytes_per_launch / (gemm_ms_per_launch * 1e-3) / 1e9
+    r = {"bound": "hbm" if hbm_bound else "mfma"}
+    if hbm_bound:
+        r.update(achieved=round(gbs, 3), peak=PEAK_HBM_GBS, unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4))
+    else:
+        r.update(achieved=round(tflops, 3), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s",
+                 frac=round(tflops / PEAK_FP8_TFLOPS, 4))
+    r.update(gemm_tflops=round(tflops, 3), gemm_gbs=round(gbs, 2),
+             frac_of_mxfp8_peak=round(tflops / PEAK_FP8_TFLOPS, 4),
+             kernel_mfma=("bf16 (exact products, v_mfma_f32_*_bf16)" if precision == "exact"
+                          else "scaled FP8 (v_mfma_scale_f32_*_f8f6f4)"),
+             kernel_mfma_peak=kernel_peak,
+             frac_of_kernel_mfma_peak=round(tflops / kernel_peak, 4),
+             frac_of_hbm=round(gbs / PEAK_HBM_GBS, 4),
+             bytes_per_launch=int(bytes_per_launch), flops_per_launch=int(flops_per_launch),
+             gemm_us_per_launch=round(gemm_ms_per_launch * 1e3, 3), launches_per_step=launches)
+    return r
+
+
+def measured_peaks(torch, dev, stream):
+    """Measured denominators: the MFMA-rate probe (scaled FP8 and bf16, no
+    memory traffic) and a 1 GiB device-to-device copy."""
+    import ctypes
+    out = {}
+    lib_path = os.path.join(ROOT, "mxfp8_block_scaled_mxgemm_amd", "libmxgemm_rate.so")
+    if os.path.exists(lib_path):
+        lib = ctypes.CDLL(lib_path)
+        lib.mxgemm_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_void_p, ctypes.c_void_p]
+        lib.mxgemm_probe_mfma_rate.restype = ctypes.c_int
+        grid, iters = 2048, 512
+        buf = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+        for kind, name, flop in ((0, "scaled_fp8_mfma_tflops", 131072), (1, "bf16_mfma_tflops", 32768)):
+            def launch():
+                rc = lib.mxgemm_probe_mfma_rate(kind, grid, iters, ctypes.c_void_p(buf.data_ptr()),
+                                                ctypes.c_void_p(stream.cuda_stream))
+                if rc != 0:
+                    raise RuntimeError(f"MFMA probe launch failed ({rc})")
+            for _ in range(3):
+                launch()
+            times = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                launch()
+                e1.record(stream)
+                e1.synchronize()
+                times.append(e0.elapsed_time(e1))
+            total = grid * 4 * iters * 16 * flop          # waves x MFMAs x FLOP
+            out[name] = round(total / (statistics.median(times) * 1e-3) / 1e12, 1)
+        out["mfma_probe"] = (f"{grid} work-groups x 4 waves, each {iters * 16} back-to-back MFMAs on "
+                             "4 independent accumulators, no memory traffic; median of 5 launches")
+        del buf
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    for _ in range(2):
+        dst.copy_(src)
+    times = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    nbytes = 2 * src.numel() * 4
+    out["copy_gbs"] = round(nbytes / (statistics.median(times) * 1e-3) / 1e9, 1)
+    out["copy"] = "1 GiB device-to-device copy (read + write bytes / time), median of 5"
+    del src, dst
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,7 +287,11 @@ def main():
     ap.add_argument("--warmup-ms", type=float, default=25.0,
                     help="untimed GPU time before each timed loop, in steps of the same kind "
                          "(at most 200 steps)")
-    ap.add_argument("--config", default="outlier_m8192_n8192_k8192", help="workload name (default outlier_m8192_n8192_k8192)")
+    ap.add_argument("--config", default="outlier_m8192_n8192_k8192", help="headline workload (default outlier_m8192_n8192_k8192)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-workload block for the other workloads")
+    ap.add_argument("--config-steps", type=int, default=20,
+                    help="timed steps per workload in the per-workload block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=25.0)
     ap.add_argument("--no-flush", action="store_true")
@@ -203,6 +299,7 @@ def main():
                     help="sustained replays while amd-smi samples the shader clock (0: off)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the second timer (replays of one HIP-graph-captured step)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured denominators")
     ap.add_argument("--tile-cfg", type=int, default=-1)
     ap.add_argument("--split", type=int, default=-1)
     ap.add_argument("--window", type=int, default=-1)
@@ -246,59 +343,29 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     pkg.load()                       # fails loudly if the HIP library is missing
-    w = inputs.WORKLOADS[args.config]
     dev = torch.device("cuda:0")
-    log(f"[bench] {args.config}: {w.describe()}")
-
-    a32, b32 = inputs.fp32_operands(w)
-    a_d = torch.from_numpy(a32).to(dev)
-    b_d = torch.from_numpy(b32).to(dev)
-    del a32, b32
-    a_q, a_s = pkg.quantize_segments(a_d, w.R, fmt=args.a_format)
-    b_q, b_s = pkg.quantize_mxfp8(b_d, fmt=args.b_format)
-    del a_d, b_d
-    c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    # identity of the run's inputs: SHA-256 of the quantised operands as they
-    # sit in device memory (A codes, A scales, B codes, B scales, in order)
-    hq = hashlib.sha256()
-    for t in (a_q, a_s, b_q, b_s):
-        hq.update(t.cpu().numpy().tobytes())
-    inputs_sha = hq.hexdigest()[:16]
-    props = torch.cuda.get_device_properties(dev)
-    import numpy as _np
-    env = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
-           "compute_units": props.multi_processor_count, "torch": torch.__version__,
-           "hip": torch.version.hip, "numpy": _np.__version__}
 
-    opts = None
     prec = pkg.PRECISION_EXACT if args.precision == "exact" else pkg.PRECISION_NATIVE
     fmts = (args.a_format, args.b_format)
-    if (args.tile_cfg >= 0 or args.split > 0 or args.window > 0 or prec != pkg.PRECISION_EXACT
-            or fmts != ("e4m3", "e4m3") or args.ring != "auto"):
-        opts = pkg.options(tile_cfg=args.tile_cfg, split=args.split, chunks_per_window=args.window,
-                           precision=prec, a_format=args.a_format, b_format=args.b_format,
-                           ring=-1 if args.ring == "auto" else args.ring)
-    g = pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts)
-    plan = g.plan.as_dict()
-    log(f"[bench] plan: {plan}")
-    stream = torch.cuda.current_stream()
 
-    def step():
-        g.run(a_q, a_s, b_q, b_s, c, stream=stream)
+    def make_inputs(w):
+        a32, b32 = inputs.fp32_operands(w)
+        a_d = torch.from_numpy(a32).to(dev)
+        b_d = torch.from_numpy(b32).to(dev)
+        del a32, b32
+        a_q, a_s = pkg.quantize_segments(a_d, w.R, fmt=args.a_format)
+        b_q, b_s = pkg.quantize_mxfp8(b_d, fmt=args.b_format)
+        del a_d, b_d
+        c = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        return a_q, a_s, b_q, b_s, c
 
     def flush_caches():
         if not args.no_flush:
             flush.fill_(1.0)
 
-    # warm-up: the first call is discarded; before each timed loop, the
-    # steps of that loop run untimed for at least --warmup steps and at
-    # least --warmup-ms of GPU time (at most 200 steps), so the timed steps
-    # do not start in the clock and power transient that follows an idle GPU
-    flush_caches()
-    step()
-    torch.cuda.synchronize()
     warm_log = {}
 
     def warm_up(run_one, label):
@@ -324,12 +391,12 @@ def main():
     # steps carry no host-enqueue gaps.  The same step captured once into a
     # HIP graph and replayed K times is timed too and reported beside it
     # (graph_ms_per_step; --no-graph skips it).
-    def timed(run_one):
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    def timed(run_one, steps):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for i in range(args.steps):
+        for i in range(steps):
             flush_caches()
             starts[i].record(stream)
             run_one()
@@ -337,8 +404,58 @@ def main():
         torch.cuda.synchronize()
         return [s.elapsed_time(e) for s, e in zip(starts, ends)], time.perf_counter() - t0
 
+    def kernel_times(g, step, n):
+        # per-kernel durations: HIP events around each launch, on extra steps
+        g.set_profiling(True)
+        for _ in range(n):
+            flush_caches()
+            step()
+        kt = g.kernel_times()
+        g.set_profiling(False)
+        torch.cuda.synchronize()
+        return kt
+
+    def make_handle(w, headline):
+        opts = None
+        if headline and (args.tile_cfg >= 0 or args.split > 0 or args.window > 0 or args.ring != "auto"):
+            opts = pkg.options(tile_cfg=args.tile_cfg, split=args.split, chunks_per_window=args.window,
+                               precision=prec, a_format=args.a_format, b_format=args.b_format,
+                               ring=-1 if args.ring == "auto" else args.ring)
+        elif prec != pkg.PRECISION_EXACT or fmts != ("e4m3", "e4m3"):
+            opts = pkg.options(precision=prec, a_format=args.a_format, b_format=args.b_format)
+        return pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts)
+
+    w = inputs.WORKLOADS[args.config]
+    log(f"[bench] {args.config}: {w.describe()}")
+    a_q, a_s, b_q, b_s, c = make_inputs(w)
+    # identity of the run's inputs: SHA-256 of the quantised operands as they
+    # sit in device memory (A codes, A scales, B codes, B scales, in order)
+    hq = hashlib.sha256()
+    for t in (a_q, a_s, b_q, b_s):
+        hq.update(t.cpu().numpy().tobytes())
+    inputs_sha = hq.hexdigest()[:16]
+    props = torch.cuda.get_device_properties(dev)
+    import numpy as _np
+    env = {"device": props.name, "arch": getattr(props, "gcnArchName", None),
+           "compute_units": props.multi_processor_count, "torch": torch.__version__,
+           "hip": torch.version.hip, "numpy": _np.__version__}
+
+    g = make_handle(w, True)
+    plan = g.plan.as_dict()
+    log(f"[bench] plan: {plan}")
+
+    def step():
+        g.run(a_q, a_s, b_q, b_s, c, stream=stream)
+
+    # warm-up: the first call is discarded; before each timed loop, the
+    # steps of that loop run untimed for at least --warmup steps and at
+    # least --warmup-ms of GPU time (at most 200 steps), so the timed steps
+    # do not start in the clock and power transient that follows an idle GPU
+    flush_caches()
+    step()
+    torch.cuda.synchronize()
     warm_up(step, "stream")
-    ms, wall = timed(step)
+    ms, wall = timed(step, args.steps)
     ms_mean = statistics.mean(ms)
     log(f"[bench] stream-issued: mean {ms_mean:.4f} ms median {statistics.median(ms):.4f} "
         f"min {min(ms):.4f} max {max(ms):.4f}")
@@ -359,7 +476,7 @@ def main():
             graph = None
     if graph is not None:
         warm_up(graph.replay, "graph")
-        gms, _ = timed(graph.replay)
+        gms, _ = timed(graph.replay, args.steps)
         graph_ms = statistics.mean(gms)
         log(f"[bench] graph replays: mean {graph_ms:.4f} ms")
 
@@ -391,38 +508,84 @@ def main():
     if graph is not None:
         del graph
 
-    # ---- per-kernel durations (HIP events around each launch) -----------
-    g.set_profiling(True)
-    nprof = max(3, min(args.steps, 10))
-    for _ in range(nprof):
-        flush_caches()
-        step()
-    kt = g.kernel_times()
-    g.set_profiling(False)
-    torch.cuda.synchronize()
+    kt = kernel_times(g, step, max(3, min(args.steps, 10)))
     gemm_ms_per_launch = kt["gemm_ms"] / kt["gemm_launches"]
     stage_ms_per_launch = kt["stage_ms"] / max(1, kt["stage_launches"])
-    flops = float(w.flops)
-    # GEMM launches per step: one per window (events protocol), or one
-    # persistent launch that also stages (flags protocol)
-    launches = 1 if plan["ring"] == pkg.RING_FLAGS else plan["windows"]
-    flops_per_launch = flops / launches
-    # algorithmic bytes of one GEMM launch (M / launches rows on average):
-    # A rows and B with their E8M0 scales, C in bfloat16
-    rows_w = w.M / launches
-    bytes_per_launch = (rows_w * w.K + w.N * w.K) * 33 / 32 + rows_w * w.N * 2
-    kernel_peak = PEAK_BF16_TFLOPS if args.precision == "exact" else PEAK_FP8_TFLOPS
-    # the roofline that bounds the launch: HBM when its arithmetic intensity
-    # is below the ridge point of the MFMA form it uses
-    hbm_bound = flops_per_launch / bytes_per_launch < kernel_peak * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if hbm_bound:
-        achieved = bytes_per_launch / (gemm_ms_per_launch * 1e-3) / 1e9
-        roof_peak, roof_unit = PEAK_HBM_GBS, "GB/s"
-    else:
-        achieved = flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
-        roof_peak, roof_unit = kernel_peak, "TFLOP/s"
-    log(f"[bench] kernels: gemm {gemm_ms_per_launch * 1e3:.2f} us/launch x{launches}, "
+    ring_flags = plan["ring"] == pkg.RING_FLAGS
+    roof = gemm_roofline(w, plan, gemm_ms_per_launch, args.precision, ring_flags)
+    log(f"[bench] kernels: gemm {gemm_ms_per_launch * 1e3:.2f} us/launch x{roof['launches_per_step']}, "
         f"stage {stage_ms_per_launch * 1e3:.2f} us/launch")
+
+    sha = kernel_source_sha()
+    traffic = load_traffic(args.config, args.precision, args.a_format, args.b_format,
+                           "flags" if ring_flags else "events", plan, sha)
+    roof["traffic"] = traffic
+    roof["stage_us_per_launch"] = round(stage_ms_per_launch * 1e3, 3)
+    roof["kernel"] = "GEMM kernel (" + ("bf16 MFMA, exact products" if args.precision == "exact"
+                                        else "scaled FP8 MFMA") + ")"
+    # the same fraction against the peak at the shader clock measured while
+    # the kernel ran (MFMA bound only)
+    roof["frac_at_measured_clock"] = (
+        round(roof["achieved"] / (roof["peak"] * telemetry["shader_clock_mhz_median"] / 2400.0), 4)
+        if telemetry and roof["bound"] == "mfma" else None)
+
+    g.close()
+    del a_q, a_s, b_q, b_s, c
+    torch.cuda.empty_cache()
+
+    # ---- the other workloads: stream timer, per-launch GEMM durations -----
+    configs = {}
+    if not args.no_configs:
+        for name, wc in inputs.WORKLOADS.items():
+            if name == args.config:
+                continue
+            log(f"[bench] workload {name}: {wc.describe()}")
+            aq, as_, bq, bs, cc = make_inputs(wc)
+            gc = make_handle(wc, False)
+            pc = gc.plan.as_dict()
+
+            def step_c():
+                gc.run(aq, as_, bq, bs, cc, stream=stream)
+
+            flush_caches()
+            step_c()
+            torch.cuda.synchronize()
+            warm_up(step_c, name)
+            cms, _ = timed(step_c, args.config_steps)
+            ktc = kernel_times(gc, step_c, 5)
+            gms_c = ktc["gemm_ms"] / ktc["gemm_launches"]
+            rc = gemm_roofline(wc, pc, gms_c, args.precision, pc["ring"] == pkg.RING_FLAGS)
+            med = statistics.median(cms)
+            mean = statistics.mean(cms)
+            configs[name] = {
+                "shape": wc.describe(),
+                "ms_per_step_mean": round(mean, 5), "ms_per_step_median": round(med, 5),
+                "ms_per_step_min": round(min(cms), 5),
+                "tflops": round(wc.flops / (mean * 1e-3) / 1e12, 3),
+                "pct_of_mxfp8_peak": round(100.0 * wc.flops / (mean * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
+                "hbm_frac_end_to_end": round(wc.algorithmic_bytes / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                "gemm_us_per_launch": rc["gemm_us_per_launch"],
+                "stage_us_per_launch": round(ktc["stage_ms"] / max(1, ktc["stage_launches"]) * 1e3, 3),
+                "roofline": {k: rc[k] for k in ("bound", "achieved", "peak", "unit", "frac",
+                                                "frac_of_kernel_mfma_peak", "frac_of_hbm",
+                                                "launches_per_step")},
+                "plan": {k: pc[k] for k in ("tile_m", "tile_n", "split", "chunks_per_window",
+                                            "windows", "grid", "ring")},
+            }
+            log(f"[bench]   mean {mean:.4f} ms, gemm {rc['gemm_us_per_launch']:.2f} us/launch, "
+                f"roofline {rc['bound']} {rc['frac']:.3f}")
+            gc.close()
+            del aq, as_, bq, bs, cc
+            torch.cuda.empty_cache()
+
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks(torch, dev, stream)
+        log(f"[bench] measured peaks: {peaks}")
+        key = "bf16_mfma_tflops" if args.precision == "exact" else "scaled_fp8_mfma_tflops"
+        if roof["bound"] == "mfma" and peaks.get("scaled_fp8_mfma_tflops"):
+            roof["frac_of_measured_mxfp8_rate"] = round(roof["gemm_tflops"] / peaks["scaled_fp8_mfma_tflops"], 4)
+            roof["frac_of_measured_kernel_mfma_rate"] = round(roof["gemm_tflops"] / peaks[key], 4)
 
     if sampler is not None:
         open(tele_path + ".stop", "w").close()
@@ -434,11 +597,7 @@ def main():
             if os.path.exists(f):
                 os.remove(f)
 
-    sha = kernel_source_sha()
-    traffic = load_traffic(args.config, args.precision, args.a_format, args.b_format,
-                           "flags" if plan["ring"] == pkg.RING_FLAGS else "events", plan, sha)
-
-    value = flops / (ms_mean * 1e-3) / 1e12
+    value = float(w.flops) / (ms_mean * 1e-3) / 1e12
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -478,27 +637,9 @@ def main():
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "warmup_run": warm_log,
         "precision": args.precision,
-        "roofline": {
-            "bound": "hbm" if hbm_bound else "mfma",
-            "kernel": "GEMM kernel (" + ("bf16 MFMA, exact products" if args.precision == "exact"
-                                         else "scaled FP8 MFMA") + ")",
-            "achieved": round(achieved, 3),
-            "peak": roof_peak,
-            "unit": roof_unit,
-            "frac": round(achieved / roof_peak, 4),
-            # the same fraction against the peak at the shader clock measured
-            # while the kernel ran (MFMA bound only)
-            "frac_at_measured_clock": (round(achieved / (roof_peak * telemetry["shader_clock_mhz_median"] / 2400.0), 4)
-                                       if telemetry and not hbm_bound else None),
-            "gemm_tflops": round(flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12, 3),
-            "frac_of_mxfp8_peak": round(flops_per_launch / (gemm_ms_per_launch * 1e-3) / 1e12
-                                        / PEAK_FP8_TFLOPS, 4),
-            "bytes_per_launch": int(bytes_per_launch),
-            "traffic": traffic,
-            "gemm_us_per_launch": round(gemm_ms_per_launch * 1e3, 3),
-            "launches_per_step": launches,
-            "stage_us_per_launch": round(stage_ms_per_launch * 1e3, 3),
-        },
+        "roofline": roof,
+        "configs": configs,
+        "measured_peaks": peaks,
         "kernel_source_sha": sha,
         "inputs_sha256": inputs_sha,
         "env": env,
@@ -511,8 +652,7 @@ def main():
                                "on the bfloat16 output (context)",
         },
     }
-    g.close()
-    del flush, a_q, a_s, b_q, b_s, c
+    del flush
     torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

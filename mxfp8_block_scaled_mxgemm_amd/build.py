@@ -34,8 +34,27 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# The benchmark's MFMA-rate probe, a library of its own (not the product).
+PROBE_SOURCE = "mfma_rate.hip"
+PROBE_LIB = os.path.join(PKG, "libmxgemm_rate.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, "-shared", "-o", PROBE_LIB + ".tmp",
+           os.path.join(CSRC, PROBE_SOURCE)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on " + PROBE_SOURCE)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; always rebuilds."""
+    """Compile every source and link the shared library (and the benchmark's
+    MFMA-rate probe); always rebuilds."""
     objs = []
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
@@ -69,6 +88,7 @@ def build(verbose: bool = False) -> str:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("link failed")
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 

@@ -34,6 +34,22 @@ def within_tol(got, ref):
     return bad, d
 
 
+def report_misses(got, ref, ms=None, ns=None, limit=12):
+    """Print the entries over tolerance (index, oracle value, GPU value,
+    difference), largest excess first."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    bad, d = within_tol(got, ref)
+    idx = np.flatnonzero(bad)
+    if idx.size == 0:
+        return
+    excess = d[idx] - (ATOL + RTOL * np.abs(ref[idx]))
+    for i in idx[np.argsort(-excess)][:limit]:
+        where = f"({int(ms[i])},{int(ns[i])})" if ms is not None else f"[{int(i)}]"
+        say(f"    miss {where}: oracle {ref[i]:.6g} gpu {got[i]:.6g} |d| {d[i]:.4g} "
+            f"tol {ATOL + RTOL * abs(ref[i]):.4g}")
+
+
 def summary(got, ref):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -127,3 +143,18 @@ def sample_entries(M, N, tile_m, tile_n, seed, count=4096):
         ns += [n] * len(rows)
         ms += list(rows)
     return np.array(ms, dtype=np.int64), np.array(ns, dtype=np.int64)
+
+
+def tail_and_random_entries(got_all, seed, frac=0.05, count=1 << 20):
+    """Entries to check on a large output: every output whose |C| (as the GPU
+    computed it) is below ``frac`` times the RMS of C -- where the absolute
+    term of the tolerance is all the budget there is -- plus ``count``
+    uniformly random entries."""
+    g = np.asarray(got_all)
+    rms = float(np.sqrt(np.mean(np.square(g, dtype=np.float64))))
+    tail = np.flatnonzero(np.abs(g) < frac * rms)
+    rng = np.random.default_rng(seed)
+    rand = rng.integers(0, g.size, count)
+    flat = np.unique(np.concatenate([tail, rand]))
+    ms, ns = np.divmod(flat, g.shape[1])
+    return ms.astype(np.int64), ns.astype(np.int64), rms, tail.size

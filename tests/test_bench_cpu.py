@@ -60,3 +60,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_roofline_against_the_metric_peak():
+    """The GEMM roofline of an MFMA-bound workload is priced against the
+    MX-FP8 peak the metric names, with the contraction's own MFMA peak
+    beside it; a skinny launch below the ridge point is priced against HBM."""
+    from mxfp8_block_scaled_mxgemm_amd import inputs
+    w = inputs.WORKLOADS["outlier_m8192_n8192_k8192"]
+    r = bench.gemm_roofline(w, {"windows": 4}, 0.2, "exact", False)
+    assert r["bound"] == "mfma" and r["peak"] == 5000.0 and r["unit"] == "TFLOP/s"
+    flops = 2 * 2048 * 8192 * 8192
+    assert abs(r["achieved"] - flops / 2e-4 / 1e12) < 1e-2
+    assert abs(r["frac"] - flops / 2e-4 / 1e12 / 5000.0) < 1e-4
+    assert r["kernel_mfma_peak"] == 2500.0
+    assert abs(r["frac_of_kernel_mfma_peak"] - 2 * r["frac"]) < 1e-3
+    s = inputs.WORKLOADS["skinny_m64_n2048_k7168"]
+    r = bench.gemm_roofline(s, {"windows": 2}, 0.01, "exact", False)
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0
+    nbytes = (32 * 7168 + 2048 * 7168) * 33 / 32 + 32 * 2048 * 2
+    assert abs(r["achieved"] - nbytes / 1e-5 / 1e9) < 1e-2

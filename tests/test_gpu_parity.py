@@ -8,8 +8,8 @@ import pytest
 
 import oracle
 from mxfp8_block_scaled_mxgemm_amd import inputs
-from gpu_common import (custom_case, sample_entries, say, summary, torch_cuda, within_tol,
-                        workload_case)
+from gpu_common import (report_misses, custom_case, sample_entries, say, summary, tail_and_random_entries,
+                        torch_cuda, within_tol, workload_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,49 +109,95 @@ def test_parity_full(name, precision):
 
 
 @pytest.mark.parametrize("name,precision", [("m4096_n4096_k7168", "exact"), ("m4096_n4096_k7168", "native"),
-                                            ("outlier_m8192_n8192_k8192", "exact"),
                                             ("example_m2048_n3584_k8192", "exact"),
                                             ("example_m2048_n3584_k8192", "native")])
-def test_parity_sampled(name, precision):
+def test_parity_full_large(name, precision):
+    """Every output of the 4096 x 4096 x 7168 workload and of the source's
+    example shape, against the full oracle (the source's own check compares
+    every element of C: verify_result.py, verify_single_rank)."""
     torch_cuda()
     case = _case(name)
-    say(f"[parity-sampled] {name} {precision} {case.w.describe()}")
-    c = case.run_gpu(opts=_opts(precision))
-    got_all = c.float().cpu().numpy()
-    assert not np.isnan(got_all).any()            # every output written
-    import mxfp8_block_scaled_mxgemm_amd as pkg
-    w = case.w
-    p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
-    ms, ns = sample_entries(w.M, w.N, p.tile_m, p.tile_n, seed=w.seed)
-    # plus every chunk boundary row
-    extra = np.arange(0, w.M, w.commMSize)
-    ms = np.concatenate([ms, extra, np.maximum(extra - 1, 0)])
-    ns = np.concatenate([ns, np.arange(len(extra)) % w.N, (np.arange(len(extra)) * 7) % w.N])
-    ref = case.oracle_entries(ms, ns)
-    got = got_all[ms, ns]
+    say(f"[parity-full-large] {name} {precision} {case.w.describe()}")
+    got = case.run_gpu(opts=_opts(precision)).float().cpu().numpy()
+    say("  oracle: full C")
+    ref = _oracle_full(case, name)
     say("  " + summary(got, ref))
     bad, _ = within_tol(got, ref)
     assert not bad.any()
 
 
-def test_native_mode_on_outlier_data_misses_only_near_zero():
-    """Characterises the native scaled MFMA on the outlier workload: its
-    dropped small products move results by a few units, so it misses the
-    tolerance only where C itself is small; the default mode must be used
-    for such data."""
+def _outlier_entries(case, got_all):
+    ms, ns, rms, ntail = tail_and_random_entries(got_all, seed=case.w.seed)
+    say(f"  {ntail} outputs with |C| < 0.05 rms (rms {rms:.4g}) + 2^20 random: {ms.size} entries")
+    ref = case.oracle_entries(ms, ns)
+    return ms, ns, ref, rms
+
+
+def test_parity_outlier_near_zero_and_random():
+    """The 8192-cube outlier workload in the default (exact) mode: every
+    output with |C| under 5% of the RMS of C -- where FP32 accumulation
+    error and the absolute tolerance are closest -- and 2^20 random ones."""
     torch_cuda()
-    import mxfp8_block_scaled_mxgemm_amd as pkg
+    case = _case("outlier_m8192_n8192_k8192")
+    say(f"[parity-outlier] exact {case.w.describe()}")
+    got_all = case.run_gpu().float().cpu().numpy()
+    assert not np.isnan(got_all).any()            # every output written
+    ms, ns, ref, _ = _outlier_entries(case, got_all)
+    got = got_all[ms, ns]
+    say("  " + summary(got, ref))
+    report_misses(got, ref, ms, ns)
+    bad, _ = within_tol(got, ref)
+    assert not bad.any()
+
+
+def _dequantized(codes, scales, fmt=oracle.E4M3):
+    """float64 values of MXFP8 codes with their per-32 scale bytes (the
+    oracle's decode table times 2^(scale - 127))."""
+    lut = (oracle.e4m3_value if fmt == oracle.E4M3 else oracle.e5m2_value)(
+        np.arange(256, dtype=np.uint8))
+    out = lut[codes]
+    out *= np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=-1)
+    return out
+
+
+def test_native_outlier_census():
+    """Census of the native scaled-MFMA mode on the outlier workload over
+    every output: its block dot drops small products next to large ones, so
+    it misses the tolerance where |C| is small.  The reference for the
+    census is the exact product in float64 (a library matmul of the oracle's
+    dequantised operands) rounded once to bfloat16 by the oracle; it is
+    checked against the oracle itself on all near-zero outputs and 2^20
+    random ones.  Not a parity claim: the default mode is used for such
+    data."""
+    torch_cuda()
     case = _case("outlier_m8192_n8192_k8192")
     w = case.w
+    say(f"[native-census] {w.describe()}")
     got_all = case.run_gpu(opts=_opts("native")).float().cpu().numpy()
-    p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
-    ms, ns = sample_entries(w.M, w.N, p.tile_m, p.tile_n, seed=w.seed)
-    ref = case.oracle_entries(ms, ns)
-    got = got_all[ms, ns]
-    bad, d = within_tol(got, ref)
-    rms = np.sqrt(np.mean(ref * ref))
-    say(f"  native outlier workload: {int(bad.sum())} of {bad.size} over tolerance; max |d| {d.max():.3g}; rms|C| {rms:.3g}")
-    assert np.all(np.abs(ref[bad]) < 0.05 * rms)
+    assert not np.isnan(got_all).any()
+    say("  float64 reference of every output")
+    a = _dequantized(np.ascontiguousarray(case.a_seg.transpose(1, 0, 2)).reshape(w.M, w.K),
+                     np.ascontiguousarray(case.s_seg.transpose(1, 0, 2)).reshape(w.M, w.K // 32))
+    b = _dequantized(case.qb, case.sb)
+    c64 = a @ b.T
+    del a, b
+    ref_all = oracle.bf16_bits_to_float(oracle.bf16_from_double(c64)).astype(np.float64)
+    del c64
+    ms, ns, ref, rms = _outlier_entries(case, got_all)
+    agree = ref_all[ms, ns] == ref
+    say(f"  float64 reference vs the oracle on {ms.size} entries: {int((~agree).sum())} differ")
+    assert agree.mean() > 1 - 1e-6
+    bad, d = within_tol(got_all, ref_all)
+    miss_ref = np.abs(ref_all[bad])
+    qs = np.percentile(miss_ref, [50, 90, 99, 100]) if miss_ref.size else [0, 0, 0, 0]
+    say(f"  native census over all {got_all.size} outputs: {int(bad.sum())} over tolerance "
+        f"({100.0 * bad.mean():.3f}%); max |d| {np.nanmax(d):.4g}; |ref| of the misses: "
+        f"median {qs[0]:.4g}, p90 {qs[1]:.4g}, p99 {qs[2]:.4g}, max {qs[3]:.4g}; rms|C| {rms:.4g}")
+    for lim in (1.0, 10.0, 100.0, 1000.0):
+        sel = np.abs(ref_all) < lim
+        say(f"    |C| < {lim:g}: {int(sel.sum())} outputs, {int((bad & sel).sum())} misses")
+    assert bad.any()                               # the characterised precision loss is real
+    assert np.all(miss_ref < 0.15 * rms)
 
 
 @pytest.mark.parametrize("precision", ["exact", "native"])
@@ -183,6 +229,11 @@ def test_small_products_next_to_large_ones(precision):
     say(f"  {precision}: C = {np.unique(got)} (exact 30)")
     if precision == "exact":
         assert np.all(got == 30.0)
+    else:
+        # the characterised loss: the seven 1 x 1 products that share a
+        # group of eight with a 448 x 448 product are dropped, twice, so
+        # only the two all-ones groups survive: 8 + 8
+        assert np.all(got == 16.0)
 
 
 ONE_SHOT_CFG, ONE_SHOT_STEPS = 6, 8
