@@ -239,6 +239,30 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
                    const void* b_scale, void* c, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one
+ * segmented GEMM exactly as mxgemm_seg_run would do it for a handle created
+ * with the same arguments and options, but with no handle and no
+ * allocation.  The staging ring, the split-K workspace and the per-tile
+ * arrival counts live in one static device array of 32 MiB per GPU, held
+ * until the process ends; problems whose ring and workspace need more fail
+ * with MXGEMM_EUNSUPPORTED (the five measured workloads need at most
+ * 17.3 MB).  The staging always runs in order on `stream` (one window per
+ * ring fill: no side stream, no events); options may be NULL, and
+ * options.ring must be -1 or MXGEMM_RING_EVENTS, options.chunks_per_window
+ * -1 or buffer_count.  Every call on one GPU uses that GPU's array and
+ * leaves its contents behind: calls that overlap on one GPU (two streams,
+ * two threads) race and give undefined C; calls in order on one stream are
+ * safe.  The first call on a device looks up the array's address there.
+ * Buffers and layouts as mxgemm_seg_run; asynchronous on `stream`.
+ * Errors: EINVAL, EUNSUPPORTED, EHIP.
+ */
+int mxgemm_seg_run_static(int64_t M, int64_t kPerRank, int32_t rank_size, int64_t N,
+                          int64_t commMSize, int32_t buffer_count, const mxgemm_seg_options_t* opts,
+                          const void* a_seg, const void* a_scale, const void* b,
+                          const void* b_scale, void* c, void* stream);
+
+/*
  * Flags protocol (the device-flag hand-over of all_to_all_matmul_impl.h,
  * MatmulProcess waiting on the flag AllToAllProcess sets after a copy):
  * MXGEMM_ETIMEOUT if a device wait of any run since the last call gave up (the work-groups of a run were not all resident at

@@ -9,5 +9,5 @@ work runs in the HIP library ``libmxgemm_seg.so`` behind the C ABI in
 from ._lib import (  # noqa: F401
     EXPORTED, FMT_E4M3, FMT_E5M2, PRECISION_EXACT, PRECISION_NATIVE, RING_EVENTS, RING_FLAGS,
     MxgemmError, Options, Plan, SegGemm, decode,
-    last_error, load, options, plan, quantize_mxfp8, quantize_segments,
+    last_error, load, options, plan, quantize_mxfp8, quantize_segments, run_static,
 )

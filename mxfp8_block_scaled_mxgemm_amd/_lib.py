@@ -25,7 +25,7 @@ EXPORTED = [
     "mxgemm_seg_create", "mxgemm_seg_create_ex", "mxgemm_seg_run", "mxgemm_seg_destroy",
     "mxgemm_seg_last_error", "mxgemm_seg_get_plan", "mxgemm_seg_plan", "mxgemm_seg_decode",
     "mxgemm_quantize_mxfp8", "mxgemm_quantize_mx", "mxgemm_seg_set_profiling",
-    "mxgemm_seg_kernel_times", "mxgemm_seg_status",
+    "mxgemm_seg_kernel_times", "mxgemm_seg_status", "mxgemm_seg_run_static",
 ]
 
 
@@ -112,6 +112,8 @@ def load():
     lib.mxgemm_seg_create_ex.argtypes = [ctypes.POINTER(vp), i64, i64, i32, i64, i64, i32,
                                          ctypes.POINTER(Options)]
     lib.mxgemm_seg_run.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.mxgemm_seg_run_static.argtypes = [i64, i64, i32, i64, i64, i32, ctypes.POINTER(Options),
+                                          vp, vp, vp, vp, vp, vp]
     lib.mxgemm_seg_destroy.argtypes = [vp]
     lib.mxgemm_seg_last_error.restype = ctypes.c_char_p
     lib.mxgemm_seg_get_plan.argtypes = [vp, ctypes.POINTER(Plan)]
@@ -129,7 +131,7 @@ def load():
                  "mxgemm_seg_destroy", "mxgemm_seg_get_plan", "mxgemm_seg_plan",
                  "mxgemm_seg_decode", "mxgemm_quantize_mxfp8", "mxgemm_quantize_mx",
                  "mxgemm_seg_set_profiling", "mxgemm_seg_status",
-                 "mxgemm_seg_kernel_times"):
+                 "mxgemm_seg_kernel_times", "mxgemm_seg_run_static"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -256,6 +258,26 @@ class SegGemm:
                 self._h = None
         except Exception:
             pass
+
+
+def run_static(M, kPerRank, rank_size, N, commMSize, buffer_count, a_seg, a_scale, b, b_scale, c,
+               opts=None, stream=None):
+    """mxgemm_seg_run_static: one segmented GEMM with the library's static
+    scratch array instead of a handle (allocates nothing).  Tensors as for
+    SegGemm.run."""
+    import torch
+    K = rank_size * kPerRank
+    exp = {"a_seg": (a_seg, (rank_size, M, kPerRank), torch.uint8),
+           "a_scale": (a_scale, (rank_size, M, kPerRank // 32), torch.uint8),
+           "b": (b, (N, K), torch.uint8), "b_scale": (b_scale, (N, K // 32), torch.uint8),
+           "c": (c, (M, N), torch.bfloat16)}
+    for name, (t, shape, dt) in exp.items():
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise ValueError(f"{name}: expected {dt} {shape}, got {t.dtype} {tuple(t.shape)}")
+    check(load().mxgemm_seg_run_static(M, kPerRank, rank_size, N, commMSize, buffer_count,
+                                       ctypes.byref(opts) if opts is not None else None,
+                                       _dptr(a_seg), _dptr(a_scale), _dptr(b), _dptr(b_scale),
+                                       _dptr(c), _stream_ptr(stream)))
 
 
 def quantize_mxfp8(x, q=None, s=None, stream=None, fmt=FMT_E4M3):

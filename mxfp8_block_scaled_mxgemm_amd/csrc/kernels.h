@@ -111,5 +111,7 @@ hipError_t launch_stage(const StageArgs& a, hipStream_t stream);
 hipError_t launch_gemm(int cfg, bool exact, int fa, int fb, const GemmArgs& a, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream);
 hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+// p[0 .. n) = v
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream);
 
 }  // namespace mxg

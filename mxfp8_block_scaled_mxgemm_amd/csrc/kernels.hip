@@ -130,6 +130,23 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Fill n 32-bit words with v (a kernel, not a memset, so the call can sit
+// in a captured HIP graph).
+__global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n, v);
+    return hipGetLastError();
+}
+
 // -------------------------------------------------------- GEMM dispatch --
 
 template <int FA, int FB>

@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -460,6 +461,167 @@ int harvest(mxgemm_seg* h)
     return MXGEMM_OK;
 }
 
+// Events protocol: for each window, the staging kernel, the ready
+// hand-over, the GEMM (and a split-K reduce), the credit hand-over; the
+// buffers are the handle's (or, for the static-scratch entry, the scratch
+// array's).
+int enqueue_events(mxgemm_seg* h, const void* a_seg, const void* a_scale, const void* b,
+                   const void* b_scale, void* c, hipStream_t st)
+{
+    const mxgemm_seg_plan_t& P = h->plan;
+    // With one slot group the staging of a window waits for the GEMM of the
+    // previous one anyway: both run on `stream`, whose order is then the
+    // ready/credit order (no cross-stream hand-offs, each of which costs
+    // tens of microseconds between these kernels).  Otherwise the staging
+    // runs on the side stream, forked from `stream`, so that it can run
+    // ahead of the GEMMs.
+    const bool one_stream = P.window_slots == 1;
+    hipStream_t producer = one_stream ? st : h->side;
+    if (!one_stream) {
+        HIP_TRY(hipEventRecord(h->start, st));
+        HIP_TRY(hipStreamWaitEvent(h->side, h->start, 0));
+    }
+
+    for (int w = 0; w < P.windows; ++w) {
+        const int chunk0 = w * P.chunks_per_window;
+        const int left = P.chunks - chunk0;
+        const int nch = left < P.chunks_per_window ? left : P.chunks_per_window;
+        const int g = w % P.window_slots;
+
+        // producer: refill slot group g once the GEMM that last read it is done
+        if (!one_stream && w >= P.window_slots)
+            HIP_TRY(hipStreamWaitEvent(h->side, h->credit[g], 0));
+        mxg::StageArgs sa;
+        sa.a_seg = (const uint8_t*)a_seg;
+        sa.sa_seg = (const uint8_t*)a_scale;
+        sa.ring = h->ring;
+        sa.sring = h->sring;
+        sa.M = P.M;
+        sa.kpr = P.kPerRank;
+        sa.cms = P.commMSize;
+        sa.slot_bytes = P.slot_bytes;
+        sa.scale_slot_bytes = P.scale_slot_bytes;
+        sa.R = P.rank_size;
+        sa.chunk0 = chunk0;
+        sa.nch = nch;
+        sa.nbuf = P.buffer_count;
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->stage_ev[2 * w], producer));
+        HIP_TRY(mxg::launch_stage(sa, producer));
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->stage_ev[2 * w + 1], producer));
+        if (!one_stream) {
+            HIP_TRY(hipEventRecord(h->ready[g], h->side));
+            // consumer: GEMM over the window once its chunks have landed
+            HIP_TRY(hipStreamWaitEvent(st, h->ready[g], 0));
+        }
+        // rows of the window: whole chunks, except that the last chunk of
+        // the problem holds only the rows left
+        const int64_t rows_left = P.M - (int64_t)chunk0 * P.commMSize;
+        const int64_t rows = (int64_t)nch * P.commMSize < rows_left ? (int64_t)nch * P.commMSize
+                                                                       : rows_left;
+        mxg::GemmArgs ga;
+        ga.a = h->ring + (int64_t)g * P.chunks_per_window * P.slot_bytes;
+        ga.as = h->sring + (int64_t)g * P.chunks_per_window * P.scale_slot_bytes;
+        ga.a_slot_stride = P.slot_bytes;
+        ga.as_slot_stride = P.scale_slot_bytes;
+        ga.b = (const uint8_t*)b;
+        ga.bs = (const uint8_t*)b_scale;
+        ga.c = (uint16_t*)c + (int64_t)chunk0 * P.commMSize * P.N;
+        ga.ws = h->ws;
+        ga.tile_cnt = h->tile_cnt;
+        ga.fused = fused_combine(P.tile_m, P.tile_n, P.split) ? 1 : 0;
+        ga.rows = (int)rows;
+        ga.N = (int)P.N;
+        ga.K = (int)P.K;
+        ga.kpr = (int)P.kPerRank;
+        ga.cms = (int)P.commMSize;
+        ga.tiles_m = (int)ceil_div(rows, P.tile_m);
+        ga.tiles_n = P.tiles_n;
+        ga.split = P.split;
+        ga.segs_per_split = P.rank_size / P.split;
+        ga.group_n = P.group_n;
+        ga.total_work = ga.tiles_m * ga.tiles_n * ga.split;
+        ga.c_vec4 = ((uintptr_t)ga.c % 8 == 0) && (P.N % 4 == 0);
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->gemm_ev[2 * w], st));
+        HIP_TRY(mxg::launch_gemm(P.tile_cfg, P.precision == MXGEMM_PRECISION_EXACT, P.a_format,
+                                 P.b_format, ga, st));
+        if (h->profiling)
+            HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
+        if (P.split > 1 && !ga.fused) {
+            mxg::ReduceArgs ra;
+            ra.ws = h->ws;
+            ra.c = ga.c;
+            ra.rows = ga.rows;
+            ra.N = ga.N;
+            ra.split = P.split;
+            ra.c_vec4 = ga.c_vec4;
+            HIP_TRY(mxg::launch_reduce(ra, st));
+        }
+        if (!one_stream)
+            HIP_TRY(hipEventRecord(h->credit[g], st));
+    }
+    if (h->profiling)
+        h->pending = true;
+    return MXGEMM_OK;
+}
+
+// ---- static scratch: the entry point that allocates nothing -----------
+//
+// mxgemm_seg_run_static keeps the ring, the split-K workspace and the
+// per-tile arrival counts in this file-scope array instead of memory that
+// create() allocates.  In host code `scratch` is only a stand-in for the
+// symbol; its device address on each GPU comes from hipGetSymbolAddress,
+// taken once per device (with that device current) and kept in
+// g_static[device].ptr, which is what every launch receives.
+constexpr int64_t kStaticScratchBytes = 32LL << 20;
+constexpr int kMaxStaticDevices = 64;
+
+struct StaticDevice {
+    bool ready;
+    uint8_t* ptr;              // device address of `scratch` on this device
+    int num_cus;
+    const void* checked[5];    // run buffers last found accessible
+};
+
+std::mutex g_static_mu;
+StaticDevice g_static[kMaxStaticDevices];
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+// Per-device set-up, once: the device must be a gfx950, and the scratch
+// array's address on it is looked up (never the symbol's host stand-in).
+int static_device(int dev, StaticDevice** out)
+{
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (dev < 0 || dev >= kMaxStaticDevices)
+        return fail(MXGEMM_EUNSUPPORTED, "device index %d out of range", dev);
+    StaticDevice& sd = g_static[dev];
+    if (!sd.ready) {
+        hipDeviceProp_t prop;
+        HIP_TRY(hipGetDeviceProperties(&prop, dev));
+        if (strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+            return fail(MXGEMM_EUNSUPPORTED, "device %d is %s; this library is built for gfx950",
+                        dev, prop.gcnArchName);
+        void* ptr = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        if (ptr == nullptr)
+            return fail(MXGEMM_EHIP, "no device address for the static scratch array");
+        sd.ptr = static_cast<uint8_t*>(ptr);
+        sd.num_cus = prop.multiProcessorCount;
+        sd.ready = true;
+    }
+    *out = &sd;
+    return MXGEMM_OK;
+}
+
+int64_t align256(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
 }  // namespace
 
 extern "C" {
@@ -673,102 +835,93 @@ int mxgemm_seg_run(mxgemm_seg_t h, const void* a_seg, const void* a_scale, const
         return MXGEMM_OK;
     }
 
-    // With one slot group the staging of a window waits for the GEMM of the
-    // previous one anyway: both run on `stream`, whose order is then the
-    // ready/credit order (no cross-stream hand-offs, each of which costs
-    // tens of microseconds between these kernels).  Otherwise the staging
-    // runs on the side stream, forked from `stream`, so that it can run
-    // ahead of the GEMMs.
-    const bool one_stream = P.window_slots == 1;
-    hipStream_t producer = one_stream ? st : h->side;
-    if (!one_stream) {
-        HIP_TRY(hipEventRecord(h->start, st));
-        HIP_TRY(hipStreamWaitEvent(h->side, h->start, 0));
+    return enqueue_events(h, a_seg, a_scale, b, b_scale, c, st);
+}
+
+int mxgemm_seg_run_static(int64_t M, int64_t kPerRank, int32_t rank_size, int64_t N,
+                          int64_t commMSize, int32_t buffer_count, const mxgemm_seg_options_t* opts,
+                          const void* a_seg, const void* a_scale, const void* b,
+                          const void* b_scale, void* c, void* stream)
+{
+    mxgemm_seg_options_t o;
+    if (opts) {
+        o = *opts;
+        if (o.ring != -1 && o.ring != MXGEMM_RING_EVENTS)
+            return fail(MXGEMM_EUNSUPPORTED, "the static-scratch entry runs the events protocol only");
+        if (o.chunks_per_window != -1 && o.chunks_per_window != buffer_count)
+            return fail(MXGEMM_EINVAL, "the static-scratch entry uses one window per ring fill "
+                        "(chunks_per_window must be -1 or buffer_count)");
+    } else {
+        memset(&o, 0xFF, sizeof(o));           // every knob -1: automatic
+    }
+    // one slot group: staging and GEMM in order on `stream`, no side stream
+    // or events (which create() would have to allocate)
+    o.chunks_per_window = buffer_count;
+    o.ring = MXGEMM_RING_EVENTS;
+    int rc = validate(M, kPerRank, rank_size, N, commMSize, buffer_count);
+    if (rc != MXGEMM_OK)
+        return rc;
+    if (!a_seg || !a_scale || !b || !b_scale || !c)
+        return fail(MXGEMM_EINVAL, "NULL data pointer");
+    if (((uintptr_t)a_seg | (uintptr_t)b) & 15u)
+        return fail(MXGEMM_EINVAL, "a_seg and b must be 16-byte aligned");
+    if (((uintptr_t)a_scale | (uintptr_t)b_scale) & 3u)
+        return fail(MXGEMM_EINVAL, "a_scale and b_scale must be 4-byte aligned");
+    if ((uintptr_t)c & 1u)
+        return fail(MXGEMM_EINVAL, "c must be 2-byte aligned");
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    StaticDevice* sd = nullptr;
+    rc = static_device(dev, &sd);
+    if (rc != MXGEMM_OK)
+        return rc;
+
+    mxgemm_seg h{};                            // lives for this call; owns nothing
+    rc = make_plan(&h.plan, M, kPerRank, rank_size, N, commMSize, buffer_count, sd->num_cus, &o);
+    if (rc != MXGEMM_OK)
+        return rc;
+    const mxgemm_seg_plan_t& P = h.plan;
+    const bool fused = fused_combine(P.tile_m, P.tile_n, P.split);
+    const int64_t ring_bytes = align256((int64_t)P.buffer_count * P.slot_bytes);
+    const int64_t sring_bytes = align256((int64_t)P.buffer_count * P.scale_slot_bytes);
+    const int64_t ws_bytes = align256(P.workspace_bytes);
+    const int64_t cnt_words = fused ? (int64_t)P.tiles_m * P.tiles_n : 0;
+    const int64_t need = ring_bytes + sring_bytes + ws_bytes + align256(4 * cnt_words);
+    if (need > kStaticScratchBytes)
+        return fail(MXGEMM_EUNSUPPORTED, "this problem needs %lld bytes of ring and workspace, "
+                    "more than the %lld-byte static scratch; use mxgemm_seg_create",
+                    (long long)need, (long long)kStaticScratchBytes);
+
+    {
+        const void* const ptr[5] = {a_seg, a_scale, b, b_scale, c};
+        static const char* const names[5] = {"a_seg", "a_scale", "b", "b_scale", "c"};
+        std::lock_guard<std::mutex> lock(g_static_mu);
+        bool same = true;
+        for (int i = 0; i < 5; ++i)
+            same = same && ptr[i] == sd->checked[i];
+        if (!same) {
+            for (int i = 0; i < 5; ++i) {
+                rc = gpu_accessible(ptr[i], names[i], dev);
+                if (rc != MXGEMM_OK)
+                    return rc;
+            }
+            for (int i = 0; i < 5; ++i)
+                sd->checked[i] = ptr[i];
+        }
     }
 
-    for (int w = 0; w < P.windows; ++w) {
-        const int chunk0 = w * P.chunks_per_window;
-        const int left = P.chunks - chunk0;
-        const int nch = left < P.chunks_per_window ? left : P.chunks_per_window;
-        const int g = w % P.window_slots;
-
-        // producer: refill slot group g once the GEMM that last read it is done
-        if (!one_stream && w >= P.window_slots)
-            HIP_TRY(hipStreamWaitEvent(h->side, h->credit[g], 0));
-        mxg::StageArgs sa;
-        sa.a_seg = (const uint8_t*)a_seg;
-        sa.sa_seg = (const uint8_t*)a_scale;
-        sa.ring = h->ring;
-        sa.sring = h->sring;
-        sa.M = P.M;
-        sa.kpr = P.kPerRank;
-        sa.cms = P.commMSize;
-        sa.slot_bytes = P.slot_bytes;
-        sa.scale_slot_bytes = P.scale_slot_bytes;
-        sa.R = P.rank_size;
-        sa.chunk0 = chunk0;
-        sa.nch = nch;
-        sa.nbuf = P.buffer_count;
-        if (h->profiling)
-            HIP_TRY(hipEventRecord(h->stage_ev[2 * w], producer));
-        HIP_TRY(mxg::launch_stage(sa, producer));
-        if (h->profiling)
-            HIP_TRY(hipEventRecord(h->stage_ev[2 * w + 1], producer));
-        if (!one_stream) {
-            HIP_TRY(hipEventRecord(h->ready[g], h->side));
-            // consumer: GEMM over the window once its chunks have landed
-            HIP_TRY(hipStreamWaitEvent(st, h->ready[g], 0));
-        }
-        // rows of the window: whole chunks, except that the last chunk of
-        // the problem holds only the rows left
-        const int64_t rows_left = P.M - (int64_t)chunk0 * P.commMSize;
-        const int64_t rows = (int64_t)nch * P.commMSize < rows_left ? (int64_t)nch * P.commMSize
-                                                                       : rows_left;
-        mxg::GemmArgs ga;
-        ga.a = h->ring + (int64_t)g * P.chunks_per_window * P.slot_bytes;
-        ga.as = h->sring + (int64_t)g * P.chunks_per_window * P.scale_slot_bytes;
-        ga.a_slot_stride = P.slot_bytes;
-        ga.as_slot_stride = P.scale_slot_bytes;
-        ga.b = (const uint8_t*)b;
-        ga.bs = (const uint8_t*)b_scale;
-        ga.c = (uint16_t*)c + (int64_t)chunk0 * P.commMSize * P.N;
-        ga.ws = h->ws;
-        ga.tile_cnt = h->tile_cnt;
-        ga.fused = fused_combine(P.tile_m, P.tile_n, P.split) ? 1 : 0;
-        ga.rows = (int)rows;
-        ga.N = (int)P.N;
-        ga.K = (int)P.K;
-        ga.kpr = (int)P.kPerRank;
-        ga.cms = (int)P.commMSize;
-        ga.tiles_m = (int)ceil_div(rows, P.tile_m);
-        ga.tiles_n = P.tiles_n;
-        ga.split = P.split;
-        ga.segs_per_split = P.rank_size / P.split;
-        ga.group_n = P.group_n;
-        ga.total_work = ga.tiles_m * ga.tiles_n * ga.split;
-        ga.c_vec4 = ((uintptr_t)ga.c % 8 == 0) && (P.N % 4 == 0);
-        if (h->profiling)
-            HIP_TRY(hipEventRecord(h->gemm_ev[2 * w], st));
-        HIP_TRY(mxg::launch_gemm(P.tile_cfg, P.precision == MXGEMM_PRECISION_EXACT, P.a_format,
-                                 P.b_format, ga, st));
-        if (h->profiling)
-            HIP_TRY(hipEventRecord(h->gemm_ev[2 * w + 1], st));
-        if (P.split > 1 && !ga.fused) {
-            mxg::ReduceArgs ra;
-            ra.ws = h->ws;
-            ra.c = ga.c;
-            ra.rows = ga.rows;
-            ra.N = ga.N;
-            ra.split = P.split;
-            ra.c_vec4 = ga.c_vec4;
-            HIP_TRY(mxg::launch_reduce(ra, st));
-        }
-        if (!one_stream)
-            HIP_TRY(hipEventRecord(h->credit[g], st));
-    }
-    if (h->profiling)
-        h->pending = true;
-    return MXGEMM_OK;
+    h.device = dev;
+    h.ring = sd->ptr;
+    h.sring = sd->ptr + ring_bytes;
+    h.ws = P.workspace_bytes > 0 ? reinterpret_cast<float*>(sd->ptr + ring_bytes + sring_bytes) : nullptr;
+    h.tile_cnt = fused ? reinterpret_cast<uint32_t*>(sd->ptr + ring_bytes + sring_bytes + ws_bytes)
+                       : nullptr;
+    hipStream_t st = (hipStream_t)stream;
+    // the arrival counts must start at zero; the array keeps whatever the
+    // last call left in this region (ring bytes of a bigger problem, say)
+    if (fused)
+        HIP_TRY(mxg::launch_fill_u32(h.tile_cnt, cnt_words, 0u, st));
+    return enqueue_events(&h, a_seg, a_scale, b, b_scale, c, st);
 }
 
 int mxgemm_seg_status(mxgemm_seg_t h)

@@ -64,6 +64,10 @@ def test_every_declaration_cites_a_page():
     for name, doc in docs.items():
         assert doc is not None, name
         flat = " ".join(re.sub(r"\n\s*\*(?!/)", " ", doc).split())
+        if name == "mxgemm_seg_run_static":
+            # not an operation of the pages: its comment names its callers
+            assert "callers that cannot allocate" in flat
+            continue
         assert any(src in flat for src in _PAGE_SOURCES), name
 
 
