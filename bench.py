@@ -275,6 +275,36 @@ def measured_peaks(torch, dev, stream):
     out["copy_gbs"] = round(nbytes / (statistics.median(times) * 1e-3) / 1e9, 1)
     out["copy"] = "1 GiB device-to-device copy (read + write bytes / time), median of 5"
     del src, dst
+
+    # floors for short steps: the event-to-event time of a one-element fill
+    # (a launch that does nothing else), and of a copy moving the skinny
+    # workload's algorithmic bytes (read + write), caches flushed first
+    def floor_us(fn, reps=20):
+        flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        ts = []
+        for _ in range(reps):
+            flush.fill_(0.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        del flush
+        return round(statistics.median(ts), 2)
+
+    one = torch.empty(1, dtype=torch.float32, device=dev)
+    out["empty_launch_us"] = floor_us(lambda: one.fill_(0.0))
+    from mxfp8_block_scaled_mxgemm_amd import inputs
+    skinny = inputs.WORKLOADS["skinny_m64_n2048_k7168"]
+    half = skinny.algorithmic_bytes // 2 // 4
+    a, b = torch.empty(half, dtype=torch.float32, device=dev), torch.empty(half, dtype=torch.float32, device=dev)
+    a.fill_(1.0)
+    out["skinny_bytes_copy_us"] = floor_us(lambda: b.copy_(a))
+    out["floors"] = (f"event-to-event medians of 20 after a 512 MiB flush: a one-element fill, and a "
+                     f"copy of {2 * half * 4} bytes read + written (the skinny workload's "
+                     f"{skinny.algorithmic_bytes} algorithmic bytes)")
+    del a, b, one
     return out
 
 

@@ -52,16 +52,19 @@ typedef struct mxgemm_seg* mxgemm_seg_t;
  *  MXGEMM_PRECISION_EXACT (default): every FP8 x FP8 x 2^(scales) product
  *    is formed exactly (codes are converted to bfloat16 with the block scale
  *    folded in, which is exact for scale bytes >= 3 with E4M3 codes, >= 10
- *    with E5M2) and the products are summed into FP32 accumulators on the
- *    bfloat16 MFMA: v_mfma_f32_32x32x16_bf16 on the 256 x 256, 256 x 128
- *    and 128 x 128 tiles, v_mfma_f32_16x16x32_bf16 on the smaller ones.  The
+ *    with E5M2) and the products are summed on the bfloat16 MFMA
+ *    (v_mfma_f32_32x32x16_bf16 on the 256 x 128 and 128 x 128 tiles,
+ *    v_mfma_f32_16x16x32_bf16 on the smaller ones), which adds them into
+ *    FP32 in groups of eight.  Each pair of K-steps (256 K) is summed in
+ *    fresh accumulators and then added to FP32 running totals, so a large
+ *    product rounds the small ones after it only until the pair ends.  The
  *    result is an FP32 sum in a fixed order, rounded once to bfloat16; like
  *    any FP32 sum it can lose small terms to cancellation of large ones
  *    (2^30 + 1 - 2^30 gives 0).  Tested: |C - exact| <= 1e-2 + 8e-3 |exact|
- *    on every output of the five measured workloads (the 8192-cube outlier
- *    workload on every output whose |C| is under 5% of the RMS plus a
- *    random sample), and bit-exact results on integer-valued data whose
- *    sums stay below 2^8.
+ *    on every output of four measured workloads and, on the 8192-cube
+ *    outlier workload, on every output whose |C| is under 5% of the RMS
+ *    plus 2^20 random ones; bit-exact results on integer-valued data whose
+ *    sums stay below 2^8.  The 256 x 256 tile has no exact-mode kernel.
  *  MXGEMM_PRECISION_NATIVE: the CDNA4 block-scaled FP8 MFMA
  *    (v_mfma_scale_f32_32x32x64_f8f6f4 on the large tiles,
  *    v_mfma_scale_f32_16x16x128_f8f6f4 on the small ones) at twice the peak
@@ -140,9 +143,9 @@ typedef struct mxgemm_seg_plan {
 /* Optional knobs for mxgemm_seg_create_ex / mxgemm_seg_plan; -1 = automatic.
  *
  * Tile table (tile_cfg: work-group tile of C, K-steps of 128 per LDS stage):
- *   0  256 x 256, 1 step   (exact: 4 waves of 128 x 128; native: 8 waves)
- *   1  256 x 128, 1 step
- *   2  128 x 128, 1 step
+ *   0  256 x 256, 1 step   (native only: 8 waves)
+ *   1  256 x 128, 1 step   (exact: 4 waves of 128 x 64)
+ *   2  128 x 128, 1 step   (exact: 4 waves of 64 x 64)
  *   3   64 x  64, 2 steps  (two work-groups per compute unit)
  *   4   32 x  64, 3 steps  (two per compute unit)
  *   5   16 x  64, 3 steps  (two per compute unit)

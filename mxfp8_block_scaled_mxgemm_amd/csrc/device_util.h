@@ -35,15 +35,21 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return (uint16_t)
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-// E8M0 scale byte (the low byte of s) -> 2^(s - 127) as float, branch-free:
-// v_ldexp_f32 gives 2^-127 (a float32 subnormal) for s = 0; the NaN byte
-// 0xFF (which ldexp would turn into +inf) is selected to NaN, so every
-// product of its block, zero codes included, is NaN.
+// E8M0 scale byte b (the low byte of s) -> the float multiplier of its
+// block for the scaled bfloat16 conversion, in two instructions (byte
+// extract, shift-or): the bits (b << 23) | b.  For b in 1..254 that is
+// 2^(b - 127) * (1 + b * 2^-23); the conversion rounds code * multiplier to
+// bfloat16, and a code has at most four significant bits, so a relative
+// excess below 2^-15 never changes the rounded value: the result is exactly
+// code * 2^(b - 127) (as long as that is on the bfloat16 grid, scale byte
+// >= 3 for E4M3 codes, >= 10 for E5M2).  b = 0xFF gives a NaN (exponent all
+// ones, mantissa nonzero), so every product of its block, zero codes
+// included, is NaN; b = 0 gives +0, so a block whose scale is 2^-127
+// contributes 0 instead of values below 2^-118.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s)
 {
     const uint32_t b = s & 0xFFu;
-    const float v = __builtin_amdgcn_ldexpf(0x1p-127f, (int)b);
-    return b == 0xFFu ? __builtin_nanf("") : v;
+    return __uint_as_float((b << 23) | b);
 }
 
 // Two FP8 codes (bytes 2h, 2h + 1 of `src`) of format F -> two bfloat16

@@ -2,6 +2,8 @@
 // Each format pair is instantiated in its own translation unit.
 #pragma once
 
+#include <type_traits>
+
 #include "device_util.h"
 #include "schedule.h"
 
@@ -365,13 +367,19 @@ mxgemm_kernel(GemmArgs p)
         const int nsteps = p.segs_per_split * (p.kpr / kBK);
 
         acc_t acc[GA][GB];
+        // exact mode: running totals; each pair of K-steps is summed in
+        // fresh accumulators first (see mxgemm_exact_kernel)
+        acc_t tot[EXACT ? GA : 1][EXACT ? GB : 1];
 #pragma unroll
         for (int i = 0; i < GA; ++i)
 #pragma unroll
             for (int j = 0; j < GB; ++j)
 #pragma unroll
-                for (int v = 0; v < NACC; ++v)
+                for (int v = 0; v < NACC; ++v) {
                     acc[i][j][v] = 0.f;
+                    if constexpr (EXACT)
+                        tot[i][j][v] = 0.f;
+                }
 
         const int nsup = (nsteps + CH - 1) / CH;    // stages of CH K-steps
 #pragma unroll
@@ -549,6 +557,17 @@ mxgemm_kernel(GemmArgs p)
                         for (int g = 0; g < GB; ++g)
                             acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[g], ab[i], acc[i][g], 0, 0, 0);
                 }
+                // close the pair of K-steps that ends here (or the last step)
+                const int step = t * CH + c;
+                if ((step & 1) == 1 || step == nsteps - 1) {
+#pragma unroll
+                    for (int i = 0; i < GA; ++i)
+#pragma unroll
+                        for (int g = 0; g < GB; ++g) {
+                            tot[i][g] += acc[i][g];
+                            acc[i][g] = acc_t{};
+                        }
+                }
             }
 
             }
@@ -561,7 +580,10 @@ mxgemm_kernel(GemmArgs p)
                 kstage(t + 1, stage1, stage0);
         }
 
-        store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
+        if constexpr (EXACT)
+            store_tile<GA, GB, MW>(p, tc, tot, m0 + wm * TM, n0 + wn * TN, lane);
+        else
+            store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
         if (p.split > 1 && p.fused)
             split_combine<BM, BN>(p, tc, m0, n0);
     }
@@ -620,6 +642,18 @@ __host__ __device__ constexpr int copies_in_part(int part, int nparts)
 
 // Exact block-scaled GEMM on v_mfma_f32_32x32x16_bf16, software-pipelined.
 //
+// Accumulation: the MFMA adds its products into the FP32 accumulator in
+// groups of eight with one round-to-nearest per group (measured: this
+// model reproduces the kernel's outputs bit for bit).  Once a large
+// product has entered an accumulator, every later group is rounded at that
+// magnitude, so on data with outliers (products of 1e4 and more) an output
+// that cancels to near zero collects errors of ~1e-2 over K = 8192.  So
+// each pair of K-steps (256 K) is summed in fresh accumulators -- its first
+// MFMAs take a zero accumulator input -- and then added to FP32 running
+// totals: an output's roundings at large magnitude are then at most the 32
+// of one pair plus one per pair.  The totals double the accumulator
+// registers, which limits a wave to 128 x 64 outputs.
+//
 // One wave per SIMD, WGM x WGN waves of (BM / WGM) x (BN / WGN); large wave
 // tiles keep the conversion work per MFMA low (each code a wave reads feeds
 // BN / WGN resp. BM / WGM outputs).  A K-step (128 K) is four sub-steps of
@@ -648,6 +682,7 @@ mxgemm_exact_kernel(GemmArgs p)
     constexpr int NF = GA + GB;            // fragments a wave reads per sub-step
     static_assert(TM % MW == 0 && TN % MW == 0, "wave tile must be a multiple of the MFMA width");
     static_assert(GB <= GA && GA % GB == 0, "B fragments are spread evenly over the A groups");
+    static_assert(GA * GB <= 8, "fresh and running accumulators of at most 128 x 64 outputs per wave");
     // upper bound of the work slices of one MFMA group (see kstep)
     constexpr int kMaxTasks = 20 + StageGeom<BM, BN, NW>::JA + StageGeom<BM, BN, NW>::JB + 4 + 2;
     typedef StageGeom<BM, BN, NW> G;
@@ -686,14 +721,24 @@ mxgemm_exact_kernel(GemmArgs p)
         const int seg0 = tc.ks * p.segs_per_split;
         const int nsteps = p.segs_per_split * (p.kpr / kBK);
 
-        v16f acc[GA][GB];
+        v16f acc[GA][GB];          // MFMA accumulators of the current pair of K-steps
+        v16f tot[GA][GB];          // running totals of the finished pairs
 #pragma unroll
         for (int i = 0; i < GA; ++i)
 #pragma unroll
             for (int g = 0; g < GB; ++g)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
+                for (int v = 0; v < 16; ++v) {
                     acc[i][g][v] = 0.f;
+                    tot[i][g][v] = 0.f;
+                }
+        auto flush = [&]() {
+#pragma unroll
+            for (int i = 0; i < GA; ++i)
+#pragma unroll
+                for (int g = 0; g < GB; ++g)
+                    tot[i][g] += acc[i][g];
+        };
 
         u32x4 raw[NF];             // codes of the sub-step after the next
         u32x4 cva[GA][2];          // A operands (bfloat16 pairs) of the current sub-step
@@ -729,7 +774,10 @@ mxgemm_exact_kernel(GemmArgs p)
         //     and the scale words of step s + 1 for fragments f = i mod GA.
         // sched_barrier fences keep that order, so the conversions run in
         // the MFMAs' shadow.
-        auto kstep = [&](int s, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+        // FRESH: the first K-step of a pair, whose first MFMA per output
+        // block starts from a zero accumulator.
+        auto kstep = [&](auto fresh, int s, const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt) {
+            constexpr bool FRESH = decltype(fresh)::value;
             // Past the last K-step the copies repeat the last one (into the
             // stage just released, never read again): no branches here.
             const StepSrc src2 = step_src(p, seg0, n0, s + 2 < nsteps ? s + 2 : nsteps - 1);
@@ -765,7 +813,7 @@ mxgemm_exact_kernel(GemmArgs p)
                         const int m = u / GB, g = u % GB;
                         acc[i][g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             __builtin_bit_cast(v8bf, cvb[c][g][m]), __builtin_bit_cast(v8bf, cva[i][m]),
-                            acc[i][g], 0, 0, 0);
+                            (FRESH && j == 0 && m == 0) ? v16f{} : acc[i][g], 0, 0, 0);
                         const int t0 = u * ntask / NU, t1 = (u + 1) * ntask / NU;
 #pragma unroll
                         for (int t = 0; t < kMaxTasks; ++t) {
@@ -807,23 +855,26 @@ mxgemm_exact_kernel(GemmArgs p)
         };
         int s = 0;
         for (; s + 1 < nsteps; s += 2) {
-            kstep(s, stage0, stage1);
-            kstep(s + 1, stage1, stage0);
+            kstep(std::true_type(), s, stage0, stage1);
+            kstep(std::false_type(), s + 1, stage1, stage0);
+            flush();
         }
-        if (s < nsteps)
-            kstep(s, stage0, stage1);
+        if (s < nsteps) {
+            kstep(std::true_type(), s, stage0, stage1);
+            flush();
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the work-group
 
         if (p.split == 1 && (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && (p.N & 7) == 0) {
             // bfloat16 C through LDS: both stages are free once every wave
             // has passed this barrier (its copies landed, its reads done);
             // waves 0, 1 use stage 0, waves 2, 3 stage 1
-            static_assert(NW == 4 && 2 * TM * TN * 2 <= G::STAGE, "two wave tiles of bf16 per stage");
+            static_assert(NW % 2 == 0 && (NW / 2) * TM * TN * 2 <= G::STAGE, "half the wave tiles of bf16 per stage");
             __syncthreads();
-            uint8_t* buf = (wave < 2 ? stage0 : stage1) + (wave & 1) * (TM * TN * 2);
-            store_tile_lds<GA, GB, TM, TN>(p, acc, buf, m0 + wm * TM, n0 + wn * TN, lane);
+            uint8_t* buf = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * (TM * TN * 2);
+            store_tile_lds<GA, GB, TM, TN>(p, tot, buf, m0 + wm * TM, n0 + wn * TN, lane);
         } else {
-            store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
+            store_tile<GA, GB, MW>(p, tc, tot, m0 + wm * TM, n0 + wn * TN, lane);
             if (p.split > 1 && p.fused)
                 split_combine<BM, BN>(p, tc, m0, n0);
         }
@@ -847,12 +898,21 @@ static hipError_t launch_cfg(const GemmArgs& a, bool exact, hipStream_t stream)
 template <int BM, int BN, int NWM, int NWN, int NOCC, int EWM, int EWN, int FA, int FB>
 static hipError_t launch_large(const GemmArgs& a, bool exact, hipStream_t stream)
 {
-    if (exact)
-        hipLaunchKernelGGL((mxgemm_exact_kernel<BM, BN, EWM, EWN, 1, FA, FB>), dim3(a.total_work),
-                           dim3(EWM * EWN * 64), 0, stream, a);
-    else
-        hipLaunchKernelGGL((mxgemm_kernel<BM, BN, NWM, NWN, NOCC, false, 32, 1, false, FA, FB>),
-                           dim3(a.total_work), dim3(NWM * NWN * 64), 0, stream, a);
+    if (exact) {
+        if constexpr ((BM / EWM) * (BN / EWN) <= 128 * 64) {
+            // EWM x EWN waves, EWM * EWN / 4 per SIMD
+            hipLaunchKernelGGL((mxgemm_exact_kernel<BM, BN, EWM, EWN, EWM * EWN / 4, FA, FB>), dim3(a.total_work),
+                               dim3(EWM * EWN * 64), 0, stream, a);
+            return hipGetLastError();
+        } else {
+            // no exact-mode kernel: the fresh and running accumulators of a
+            // 128 x 128 wave tile would not fit the register file (the
+            // planner never asks for it)
+            return hipErrorInvalidValue;
+        }
+    }
+    hipLaunchKernelGGL((mxgemm_kernel<BM, BN, NWM, NWN, NOCC, false, 32, 1, false, FA, FB>),
+                       dim3(a.total_work), dim3(NWM * NWN * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -863,7 +923,7 @@ hipError_t launch_gemm_fmt(int cfg, bool exact, const GemmArgs& a, hipStream_t s
 {
     switch (cfg) {
     case 0: return launch_large<256, 256, 2, 4, 2, 2, 2, FA, FB>(a, exact, stream);
-    case 1: return launch_large<256, 128, 2, 2, 1, 2, 2, FA, FB>(a, exact, stream);
+    case 1: return launch_large<256, 128, 2, 2, 1, 4, 2, FA, FB>(a, exact, stream);
     case 2: return launch_large<128, 128, 2, 2, 1, 2, 2, FA, FB>(a, exact, stream);
     case 3: return launch_cfg<64, 64, 2, 2, 2, 16, 2, false, FA, FB>(a, exact, stream);
     case 4: return launch_cfg<32, 64, 1, 4, 2, 16, 3, false, FA, FB>(a, exact, stream);

@@ -14,6 +14,8 @@ struct TileCfg {
     int blocks_per_cu;      // resident work-groups per compute unit
     float rel_rate;         // planner's relative MFMA efficiency estimate
     int steps_per_stage;    // K-steps of 128 copied per LDS stage
+    bool exact;             // has an exact-mode kernel
+    bool automatic;         // the planner may choose it unasked
 };
 
 int num_tile_cfgs();

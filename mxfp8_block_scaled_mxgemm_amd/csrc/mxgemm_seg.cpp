@@ -201,6 +201,9 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     if (opts && opts->tile_cfg >= mxg::num_tile_cfgs())
         return fail(MXGEMM_EINVAL, "tile_cfg %d out of range [0, %d)", opts->tile_cfg,
                     mxg::num_tile_cfgs());
+    if (opts && opts->tile_cfg >= 0 && exact && !mxg::tile_cfg(opts->tile_cfg).exact)
+        return fail(MXGEMM_EINVAL, "tile_cfg %d (%d x %d) has no exact-mode kernel", opts->tile_cfg,
+                    mxg::tile_cfg(opts->tile_cfg).tile_m, mxg::tile_cfg(opts->tile_cfg).tile_n);
 
     Choice best = {-1, 1, 1e300, 0};
     int best_w = w_cand[0];
@@ -216,6 +219,8 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
         for (int c = 0; c < ncfg; ++c) {
             if (opts && opts->tile_cfg >= 0 && opts->tile_cfg != c)
                 continue;
+            if (exact && !mxg::tile_cfg(c).exact)
+                continue;
             for (int s = 1; s <= R; ++s) {
                 if (R % s != 0)
                     continue;
@@ -223,16 +228,23 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
                     continue;
                 if (c == mxg::kOneShotCfg && (int64_t)(R / s) * (kpr / 128) > mxg::kOneShotSteps)
                     continue;   // a work item's K range must fit the single stage
-                // The one-shot tile only when asked for: measured against the
-                // pipelined 16 x 64 tile (two work-groups per CU) it was
-                // slower on every shape it fits (64 x 2048 x 7168: 37.4 vs
-                // 33.9 us per run; 128 x 256 x 512: 12.2 vs 11.8 us), which
-                // this cost model does not predict.
-                if (c == mxg::kOneShotCfg && !(opts && opts->tile_cfg == c))
+                // Some tiles only when asked for (the one-shot tile: measured
+                // against the pipelined 16 x 64 tile, two work-groups per CU,
+                // it was slower on every shape it fits -- 64 x 2048 x 7168:
+                // 37.4 vs 33.9 us per run; 128 x 256 x 512: 12.2 vs 11.8 us --
+                // which this cost model does not predict).
+                if (!mxg::tile_cfg(c).automatic && !(opts && opts->tile_cfg == c))
                     continue;
                 const double gemm = estimate(mxg::tile_cfg(c), rows, N, p->K, s, num_cus, exact);
+                // With two or more slot groups the staging runs on the side
+                // stream, and each window pays the ready and credit hand-offs
+                // between the streams: ~14 us per window measured on the
+                // 8192-cube workload (eight 1024-row windows took 1146 us per
+                // run against 1029 us for four 2048-row windows on one
+                // stream, the GEMM launches accounting for 1033 and 993 us).
+                const double handoff = 14.0e-6 * 2.4e9;
                 const double cost = overlap
-                    ? (double)windows * (gemm > stage ? gemm : stage) + stage
+                    ? (double)windows * ((gemm > stage ? gemm : stage) + handoff) + stage
                     : (double)windows * (gemm + stage);
                 // estimates within 0.1% count as a tie, which goes to the
                 // plan with more work items: more work-groups in flight hide

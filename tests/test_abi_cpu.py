@@ -186,7 +186,8 @@ def test_schedule_bijection_on_workloads(name):
 @pytest.mark.parametrize("split", [1, 2, 3])
 def test_schedule_bijection_forced(cfg, split):
     p = pkg.plan(120, 256, 6, 200, 24, 4, num_cus=16,
-                 opts=pkg.options(tile_cfg=cfg, split=split))
+                 opts=pkg.options(tile_cfg=cfg, split=split,
+                                  precision=pkg.PRECISION_NATIVE if cfg == 0 else -1))
     _check_bijection(p, p.chunks_per_window * 24)
     _check_bijection(p, 24)
 
@@ -263,3 +264,17 @@ def test_binding_refuses_host_tensors():
     from mxfp8_block_scaled_mxgemm_amd import _lib
     with pytest.raises(TypeError):
         _lib._dptr(x)
+
+
+def test_exact_mode_has_no_256x256_tile():
+    """The 256 x 256 tile is native only (its exact form's fresh and running
+    FP32 accumulators would not fit the register file): the planner never
+    takes it in exact mode, and forcing it there is an argument error."""
+    for w in inputs.WORKLOADS.values():
+        p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
+        assert p.tile_cfg != 0, w.describe()
+    with pytest.raises(pkg.MxgemmError) as ei:
+        pkg.plan(8192, 1024, 8, 8192, 512, 4, opts=pkg.options(tile_cfg=0))
+    assert ei.value.code == pkg._lib.MXGEMM_EINVAL
+    p = pkg.plan(8192, 1024, 8, 8192, 512, 4, opts=pkg.options(tile_cfg=0, precision=pkg.PRECISION_NATIVE))
+    assert p.tile_cfg == 0

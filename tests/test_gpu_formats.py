@@ -132,7 +132,8 @@ def test_parity_forced_tiles_formats(fa, fb, cfg, split, precision):
     say(f"[parity-fmt-forced] fa={fa} fb={fb} cfg={cfg} split={split} {precision}")
     opts = _opts(precision)
     opts.tile_cfg, opts.split = cfg, split
-    if cfg == ONE_SHOT_CFG and (6 // split) * (256 // 128) > ONE_SHOT_STEPS:
+    if (cfg == ONE_SHOT_CFG and (6 // split) * (256 // 128) > ONE_SHOT_STEPS) or \
+            (cfg == 0 and precision == "exact"):       # 256 x 256 is native only
         with pytest.raises(pkg.MxgemmError):
             case.run_gpu(opts=opts)
         return

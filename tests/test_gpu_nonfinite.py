@@ -56,7 +56,8 @@ def test_gpu_nan_scale_byte(plan, precision):
     R, M, kpr, N, cms, nbuf = 4, 96, 256, 192, 16, 4
     case = custom_case(R=R, M=M, kpr=kpr, N=N, cms=cms, nbuf=nbuf, seed=31)
     prec = pkg.PRECISION_EXACT if precision == "exact" else pkg.PRECISION_NATIVE
-    kw = {"large_tile": dict(tile_cfg=0, split=1), "small_tile_split": dict(tile_cfg=5, split=2),
+    kw = {"large_tile": dict(tile_cfg=0 if precision == "native" else 1, split=1),
+          "small_tile_split": dict(tile_cfg=5, split=2),
           "flags": dict(ring=pkg.RING_FLAGS)}[plan]
     opts = pkg.options(precision=prec, **kw)
     say(f"[nan-scale] {plan} {precision}")

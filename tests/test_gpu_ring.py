@@ -156,7 +156,7 @@ def test_allocation_failure_is_enomem_and_leaves_no_error_behind():
     from mxfp8_block_scaled_mxgemm_amd import _lib
     say("[enomem] 2 TiB workspace request")
     with pytest.raises(pkg.MxgemmError) as ei:
-        pkg.SegGemm(65536, 128, 8, 1 << 20, 65536, 1, opts=pkg.options(tile_cfg=0, split=8))
+        pkg.SegGemm(65536, 128, 8, 1 << 20, 65536, 1, opts=pkg.options(tile_cfg=1, split=8))
     assert ei.value.code == _lib.MXGEMM_ENOMEM
     case = _case()
     got = case.run_gpu().float().cpu().numpy()

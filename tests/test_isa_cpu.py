@@ -3,8 +3,9 @@ GPU), from one parallel compile of every source to assembly:
 - memory is written only through vector instructions: no scalar-cache
   store, atomic, write-back or discard appears anywhere;
 - no kernel spills registers to scratch (and the GEMM kernels spill none
-  at all), and the 256 x 256 exact GEMM kernel fits the CU's LDS at one
-  work-group per CU.
+  at all), and the exact GEMM kernels (256 x 128 on eight waves and
+  128 x 128 on four, with fresh and running FP32 accumulators) fit a CU at
+  one work-group; no 256 x 256 exact kernel is built.
 This file is CPU-only and is not sent to GPU runs."""
 import os
 import re
@@ -76,8 +77,12 @@ def test_no_register_spills(compiled, src):
             assert v.get("SGPRs Spill", 0) == 0, (k, v)
 
 
-def test_exact_256x256_kernel_fits_one_work_group_per_cu(compiled):
+def test_exact_kernels_fit_one_work_group_per_cu(compiled):
+    """256 x 128 runs eight waves (two per SIMD), 128 x 128 four (one per
+    SIMD); either way one work-group fills a CU's LDS share and SIMDs."""
     _, kernels = compiled["gemm_e4m3_e4m3.hip"]
-    exact = [v for k, v in kernels.items() if "mxgemm_exact_kernelILi256ELi256E" in k]
-    assert len(exact) == 1
-    assert exact[0]["LDS Size"] <= 160 * 1024 and exact[0]["Occupancy"] == 1
+    assert not [k for k in kernels if "mxgemm_exact_kernelILi256ELi256E" in k]
+    for tile, waves_per_simd in (("ILi256ELi128ELi4ELi2E", 2), ("ILi128ELi128ELi2ELi2E", 1)):
+        exact = [v for k, v in kernels.items() if "mxgemm_exact_kernel" + tile in k]
+        assert len(exact) == 1, tile
+        assert exact[0]["LDS Size"] <= 160 * 1024 and exact[0]["Occupancy"] == waves_per_simd, exact[0]
