@@ -144,7 +144,7 @@ typedef struct mxgemm_seg_plan {
  *
  * Tile table (tile_cfg: work-group tile of C, K-steps of 128 per LDS stage):
  *   0  256 x 256, 1 step   (native only: 8 waves)
- *   1  256 x 128, 1 step   (exact: 4 waves of 128 x 64)
+ *   1  256 x 128, 1 step   (native: 4 waves of 128 x 64; exact: 8 of 64 x 64)
  *   2  128 x 128, 1 step   (exact: 4 waves of 64 x 64)
  *   3   64 x  64, 2 steps  (two work-groups per compute unit)
  *   4   32 x  64, 3 steps  (two per compute unit)

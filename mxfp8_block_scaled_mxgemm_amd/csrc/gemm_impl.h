@@ -514,49 +514,57 @@ mxgemm_kernel(GemmArgs p)
                     __builtin_amdgcn_sched_barrier(0);
                 }
             } else {
-                // Exact, 16 x 16 x 32 bf16: each MX block j is one MFMA.
-                // Lane group q takes 8 codes of block j (K [32j + 8q, +8)),
-                // converted to bfloat16 with the block's scale folded in
-                // (exact: 4-bit significands times a power of two).  A and
-                // B use the same K assignment, so every product pairs
-                // correctly; products are exact in the MFMA and summed with
-                // FP32-grade precision.
-                // All four blocks' codes are read first: one LDS round
-                // trip per K-step (these small tiles have few MFMAs to hide
-                // latency behind).
+                // Exact, 16 x 16 x 32 bf16, four MFMAs per (A group, B
+                // group) per K-step: MFMA m (0, 1) of half s (0, 1) takes,
+                // in lane group q = lane / 16, the codes of K [64s + 16q +
+                // 8m, +8).  So one 16-byte read of logical chunk 4s + q
+                // feeds both MFMAs of a half, and a read instruction's
+                // lanes of rows 0..7 land on eight different 16-byte bank
+                // groups (8-byte reads of two rows 8 apart share one).  A
+                // and B use the same K assignment, so every product pairs
+                // correctly; each lane folds in the scale of its own MX
+                // block, 2s + q / 2.  Products are exact in the MFMA and
+                // summed with FP32-grade precision.  Both halves' codes are
+                // read first: one LDS round trip per K-step (these small
+                // tiles have few MFMAs to hide latency behind).
                 uint32_t sa_w[GA], sb_w[GB];
-                u32x2 rb[4][GB], ra[4][GA];
+                u32x4 rb[2][GB], ra[2][GA];
+                const int sshift = 8 * (lq >> 1);
 #pragma unroll
                 for (int g = 0; g < GB; ++g)
-                    sb_w[g] = *reinterpret_cast<const uint32_t*>(psb + g * MW * 4);
+                    sb_w[g] = *reinterpret_cast<const uint32_t*>(psb + g * MW * 4) >> sshift;
 #pragma unroll
                 for (int i = 0; i < GA; ++i)
-                    sa_w[i] = *reinterpret_cast<const uint32_t*>(psa + i * MW * 4);
+                    sa_w[i] = *reinterpret_cast<const uint32_t*>(psa + i * MW * 4) >> sshift;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int lane_off = chunk(2 * j + (lq >> 1)) + (lq & 1) * 8;
+                for (int s = 0; s < 2; ++s) {
+                    const int lane_off = chunk(4 * s + lq);
 #pragma unroll
                     for (int g = 0; g < GB; ++g)
-                        rb[j][g] = *reinterpret_cast<const u32x2*>(pb + g * MW * kBK + lane_off);
+                        rb[s][g] = *reinterpret_cast<const u32x4*>(pb + g * MW * kBK + lane_off);
 #pragma unroll
                     for (int i = 0; i < GA; ++i)
-                        ra[j][i] = *reinterpret_cast<const u32x2*>(pa + i * MW * kBK + lane_off);
+                        ra[s][i] = *reinterpret_cast<const u32x4*>(pa + i * MW * kBK + lane_off);
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    v8bf bb[GB], ab[GA];
+                for (int s = 0; s < 2; ++s)
 #pragma unroll
-                    for (int g = 0; g < GB; ++g)
-                        bb[g] = fp8x8_to_bf16<FB>(rb[j][g], e8m0_to_f32(sb_w[g] >> (8 * j)));
-#pragma unroll
-                    for (int i = 0; i < GA; ++i)
-                        ab[i] = fp8x8_to_bf16<FA>(ra[j][i], e8m0_to_f32(sa_w[i] >> (8 * j)));
-#pragma unroll
-                    for (int i = 0; i < GA; ++i)
+                    for (int m = 0; m < 2; ++m) {
+                        v8bf bb[GB], ab[GA];
 #pragma unroll
                         for (int g = 0; g < GB; ++g)
-                            acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[g], ab[i], acc[i][g], 0, 0, 0);
-                }
+                            bb[g] = fp8x8_to_bf16<FB>(m ? u32x2{rb[s][g].z, rb[s][g].w} : u32x2{rb[s][g].x, rb[s][g].y},
+                                                      e8m0_to_f32(sb_w[g] >> (16 * s)));
+#pragma unroll
+                        for (int i = 0; i < GA; ++i)
+                            ab[i] = fp8x8_to_bf16<FA>(m ? u32x2{ra[s][i].z, ra[s][i].w} : u32x2{ra[s][i].x, ra[s][i].y},
+                                                      e8m0_to_f32(sa_w[i] >> (16 * s)));
+#pragma unroll
+                        for (int i = 0; i < GA; ++i)
+#pragma unroll
+                            for (int g = 0; g < GB; ++g)
+                                acc[i][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bb[g], ab[i], acc[i][g], 0, 0, 0);
+                    }
                 // close the pair of K-steps that ends here (or the last step)
                 const int step = t * CH + c;
                 if ((step & 1) == 1 || step == nsteps - 1) {
