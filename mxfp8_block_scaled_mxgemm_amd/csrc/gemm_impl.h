@@ -588,6 +588,20 @@ mxgemm_kernel(GemmArgs p)
                 kstage(t + 1, stage1, stage0);
         }
 
+        if constexpr (!EXACT && MW == 32 && !ONE) {
+            // Native large tiles: bfloat16 C as whole rows through LDS, as
+            // in the exact kernel (the stages are free: every wave has
+            // passed the last stage's barrier); waves 0 .. NW/2 - 1 use
+            // stage 0, the others stage 1.
+            static_assert(NW % 2 == 0 && (NW / 2) * TM * TN * 2 <= CH * G::STAGE,
+                          "half the wave tiles of bf16 per stage");
+            if (p.split == 1 && (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && (p.N & 7) == 0) {
+                __syncthreads();
+                uint8_t* buf = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * (TM * TN * 2);
+                store_tile_lds<GA, GB, TM, TN>(p, acc, buf, m0 + wm * TM, n0 + wn * TN, lane);
+                return;
+            }
+        }
         if constexpr (EXACT)
             store_tile<GA, GB, MW>(p, tc, tot, m0 + wm * TM, n0 + wn * TN, lane);
         else
@@ -679,12 +693,22 @@ __host__ __device__ constexpr int copies_in_part(int part, int nparts)
 // reuses the stage just finished, and sub-steps 2 and 3 read the first
 // codes of step s + 1.  The MFMAs take the B fragment as their first
 // operand, so a lane's accumulators hold four consecutive columns of C.
-template <int BM, int BN, int WGM, int WGN, int OCC, int FA, int FB>
-__global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+//
+// K groups (WGK > 1): WGK groups of WGM x WGN waves share the tile, group k
+// taking K-steps k, k + WGK, k + 2 WGK, ... of the work item, so a small
+// tile still gets large wave tiles (few conversions per MFMA) and enough
+// waves.  A stage then holds WGK K-steps, one per group, each copied by its
+// own group; every wave runs the pipeline above on its group's K-steps
+// (pairs of them summed fresh).  At the end groups 1 .. WGK - 1 pass their
+// totals through LDS and group 0 adds them in group order and stores the
+// tile.  The work item's K-steps must be a multiple of WGK.
+template <int BM, int BN, int WGM, int WGN, int WGK, int OCC, int FA, int FB>
+__global__ void __launch_bounds__(WGM * WGN * WGK * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 mxgemm_exact_kernel(GemmArgs p)
 {
     constexpr int MW = 32;
-    constexpr int NW = WGM * WGN;
+    constexpr int NWG = WGM * WGN;         // waves of one K group
+    constexpr int NW = NWG * WGK;
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int GA = TM / MW, GB = TN / MW;
     constexpr int NF = GA + GB;            // fragments a wave reads per sub-step
@@ -692,25 +716,27 @@ mxgemm_exact_kernel(GemmArgs p)
     static_assert(GB <= GA && GA % GB == 0, "B fragments are spread evenly over the A groups");
     static_assert(GA * GB <= 8, "fresh and running accumulators of at most 128 x 64 outputs per wave");
     // upper bound of the work slices of one MFMA group (see kstep)
-    constexpr int kMaxTasks = 20 + StageGeom<BM, BN, NW>::JA + StageGeom<BM, BN, NW>::JB + 4 + 2;
-    typedef StageGeom<BM, BN, NW> G;
+    constexpr int kMaxTasks = 20 + StageGeom<BM, BN, NWG>::JA + StageGeom<BM, BN, NWG>::JB + 4 + 2;
+    typedef StageGeom<BM, BN, NWG> G;      // one K-step, copied by one K group
 
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[G::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[G::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[WGK * G::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[WGK * G::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int wk = wave / NWG, wl = wave % NWG;                  // K group, wave in the group
+    const int wm = wl / WGN, wn = wl % WGN;
     const int lr = lane & 31, lq = lane >> 5;
+    const int ksub = wk * G::STAGE;        // the group's K-step within a stage
 
     // Byte offsets in a stage of the lane's first A and B fragment rows and
     // of their scale words; fragment bases are multiples of 32 rows, so the
     // swizzle key of every row is that of lr.
-    const int a_row = (wm * TM + lr) * kBK;
-    const int b_row = G::A_BYTES + (wn * TN + lr) * kBK;
-    const int sa_row = G::SA_OFF + (wm * TM + lr) * 4;
-    const int sb_row = G::SB_OFF + (wn * TN + lr) * 4;
+    const int a_row = ksub + (wm * TM + lr) * kBK;
+    const int b_row = ksub + G::A_BYTES + (wn * TN + lr) * kBK;
+    const int sa_row = ksub + G::SA_OFF + (wm * TM + lr) * 4;
+    const int sb_row = ksub + G::SB_OFF + (wn * TN + lr) * 4;
     auto frag_off = [&](int f) { return f < GA ? a_row + f * MW * kBK : b_row + (f - GA) * MW * kBK; };
     auto scale_off = [&](int f) { return f < GA ? sa_row + f * MW * 4 : sb_row + (f - GA) * MW * 4; };
     auto chunk_off = [&](int j) { return swz_t<MW>(lr, 2 * j + lq) * 16; };
@@ -724,10 +750,12 @@ mxgemm_exact_kernel(GemmArgs p)
     {
         const TileCoord tc = decode_work(w, p.tiles_m, p.tiles_n, p.split, p.group_n);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
-        CopyOffsets<BM, BN, NW, MW> co;
-        copy_offsets(p, m0, n0, wave, lane, co);
+        CopyOffsets<BM, BN, NWG, MW> co;
+        copy_offsets(p, m0, n0, wl, lane, co);
         const int seg0 = tc.ks * p.segs_per_split;
-        const int nsteps = p.segs_per_split * (p.kpr / kBK);
+        // the group's K-steps: s -> work-item K-step WGK s + wk
+        const int nsteps = p.segs_per_split * (p.kpr / kBK) / WGK;
+        auto src_of = [&](int s) { return step_src(p, seg0, n0, WGK * s + wk); };
 
         v16f acc[GA][GB];          // MFMA accumulators of the current pair of K-steps
         v16f tot[GA][GB];          // running totals of the finished pairs
@@ -753,11 +781,11 @@ mxgemm_exact_kernel(GemmArgs p)
         u32x4 cvb[2][GB][2];       // B operands, by sub-step parity
         uint32_t sw[NF];           // scale words (4 MX blocks) of a K-step
 
-        copy_issue(co, step_src(p, seg0, n0, 0), stage0, wave);
+        copy_issue(co, src_of(0), stage0 + ksub, wl);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (nsteps > 1)
-            copy_issue(co, step_src(p, seg0, n0, 1), stage1, wave);
+            copy_issue(co, src_of(1), stage1 + ksub, wl);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
             sw[f] = *reinterpret_cast<const uint32_t*>(stage0 + scale_off(f));
@@ -788,7 +816,7 @@ mxgemm_exact_kernel(GemmArgs p)
             constexpr bool FRESH = decltype(fresh)::value;
             // Past the last K-step the copies repeat the last one (into the
             // stage just released, never read again): no branches here.
-            const StepSrc src2 = step_src(p, seg0, n0, s + 2 < nsteps ? s + 2 : nsteps - 1);
+            const StepSrc src2 = src_of(s + 2 < nsteps ? s + 2 : nsteps - 1);
             uint32_t swn[NF];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -811,7 +839,7 @@ mxgemm_exact_kernel(GemmArgs p)
                     constexpr int RB = GA / GB;                       // groups per B fragment
                     const int nbf = i % RB == 0 ? 1 : 0;              // B fragment i / RB is the group's
                     const int gb = i / RB;
-                    const int ncopy = j == 2 ? copies_in_part<BM, BN, NW>(i, GA) : 0;
+                    const int ncopy = j == 2 ? copies_in_part<BM, BN, NWG>(i, GA) : 0;
                     const int nsw = j == 2 ? 1 + (i + GA < NF ? 1 : 0) : 0;   // fragments i, i + GA
                     const int ntask = 10 * (1 + nbf) + ncopy + nsw;
                     u32x4 cva_n[2];
@@ -843,7 +871,7 @@ mxgemm_exact_kernel(GemmArgs p)
                                 else
                                     raw[GA + gb] = *reinterpret_cast<const u32x4*>(src + frag_off(GA + gb) + coff);
                             } else if (t < 10 * (1 + nbf) + ncopy) {   // copies of step s + 2
-                                copy_one(co, src2, const_cast<uint8_t*>(cur), wave, i, GA, t - 10 * (1 + nbf));
+                                copy_one(co, src2, const_cast<uint8_t*>(cur) + ksub, wl, i, GA, t - 10 * (1 + nbf));
                             } else {                                   // scale words of step s + 1
                                 const int f2 = i + GA * (t - 10 * (1 + nbf) - ncopy);
                                 swn[f2] = *reinterpret_cast<const uint32_t*>(nxt + scale_off(f2));
@@ -873,16 +901,64 @@ mxgemm_exact_kernel(GemmArgs p)
         }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the work-group
 
+        if constexpr (WGK > 1) {
+            // Groups 1 .. WGK - 1 leave their totals in stage 0 (elements
+            // 4q .. 4q + 3 of accumulator block b of a lane as one 16-byte
+            // piece at float (b * 4 + q) * 256 + 4 * lane of the wave's
+            // slot), group 0 adds them in group order.
+            static_assert((WGK - 1) * NWG * TM * TN * 4 <= WGK * G::STAGE, "totals of the other groups fit a stage");
+            float* red = reinterpret_cast<float*>(stage0);
+            __syncthreads();                               // every wave has read its last codes
+            if (wk > 0) {
+                float* slot = red + ((wk - 1) * NWG + wl) * (TM * TN);
+#pragma unroll
+                for (int i = 0; i < GA; ++i)
+#pragma unroll
+                    for (int g = 0; g < GB; ++g)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<v4f*>(slot + ((i * GB + g) * 4 + q) * 256 + 4 * lane) =
+                                v4f{tot[i][g][4 * q], tot[i][g][4 * q + 1], tot[i][g][4 * q + 2], tot[i][g][4 * q + 3]};
+            }
+            __syncthreads();
+            if (wk == 0) {
+#pragma unroll 1
+                for (int k = 1; k < WGK; ++k) {
+                    const float* slot = red + ((k - 1) * NWG + wl) * (TM * TN);
+#pragma unroll
+                    for (int i = 0; i < GA; ++i)
+#pragma unroll
+                        for (int g = 0; g < GB; ++g)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const v4f x = *reinterpret_cast<const v4f*>(slot + ((i * GB + g) * 4 + q) * 256 + 4 * lane);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e)
+                                    tot[i][g][4 * q + e] += x[e];
+                            }
+                }
+            }
+        }
         if (p.split == 1 && (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && (p.N & 7) == 0) {
             // bfloat16 C through LDS: both stages are free once every wave
-            // has passed this barrier (its copies landed, its reads done);
-            // waves 0, 1 use stage 0, waves 2, 3 stage 1
-            static_assert(NW % 2 == 0 && (NW / 2) * TM * TN * 2 <= G::STAGE, "half the wave tiles of bf16 per stage");
-            __syncthreads();
-            uint8_t* buf = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * (TM * TN * 2);
-            store_tile_lds<GA, GB, TM, TN>(p, tot, buf, m0 + wm * TM, n0 + wn * TN, lane);
+            // has passed this barrier (its copies landed, its reads done).
+            // One K group: waves 0 .. NW/2 - 1 use stage 0, the others stage
+            // 1; several: group 0 stores, through stage 1 (stage 0 holds the
+            // other groups' totals, read until now).
+            if constexpr (WGK == 1) {
+                static_assert(NW % 2 == 0 && (NW / 2) * TM * TN * 2 <= G::STAGE, "half the wave tiles of bf16 per stage");
+                __syncthreads();
+                uint8_t* buf = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * (TM * TN * 2);
+                store_tile_lds<GA, GB, TM, TN>(p, tot, buf, m0 + wm * TM, n0 + wn * TN, lane);
+            } else {
+                static_assert(NWG * TM * TN * 2 <= WGK * G::STAGE, "bf16 wave tiles of one group fit a stage");
+                if (wk == 0)
+                    store_tile_lds<GA, GB, TM, TN>(p, tot, stage1 + wl * (TM * TN * 2), m0 + wm * TM,
+                                                   n0 + wn * TN, lane);
+            }
         } else {
-            store_tile<GA, GB, MW>(p, tc, tot, m0 + wm * TM, n0 + wn * TN, lane);
+            if (wk == 0)
+                store_tile<GA, GB, MW>(p, tc, tot, m0 + wm * TM, n0 + wn * TN, lane);
             if (p.split > 1 && p.fused)
                 split_combine<BM, BN>(p, tc, m0, n0);
         }
@@ -909,7 +985,7 @@ static hipError_t launch_large(const GemmArgs& a, bool exact, hipStream_t stream
     if (exact) {
         if constexpr ((BM / EWM) * (BN / EWN) <= 128 * 64) {
             // EWM x EWN waves, EWM * EWN / 4 per SIMD
-            hipLaunchKernelGGL((mxgemm_exact_kernel<BM, BN, EWM, EWN, EWM * EWN / 4, FA, FB>), dim3(a.total_work),
+            hipLaunchKernelGGL((mxgemm_exact_kernel<BM, BN, EWM, EWN, 1, EWM * EWN / 4, FA, FB>), dim3(a.total_work),
                                dim3(EWM * EWN * 64), 0, stream, a);
             return hipGetLastError();
         } else {
@@ -937,6 +1013,13 @@ hipError_t launch_gemm_fmt(int cfg, bool exact, const GemmArgs& a, hipStream_t s
     case 4: return launch_cfg<32, 64, 1, 4, 2, 16, 3, false, FA, FB>(a, exact, stream);
     case 5: return launch_cfg<16, 64, 1, 4, 2, 16, 3, false, FA, FB>(a, exact, stream);
     case 6: return launch_cfg<32, 64, 1, 4, 1, 16, kOneShotSteps, true, FA, FB>(a, exact, stream);
+    case 7:
+        // exact only: 64 x 64 in four K groups of one 64 x 64 wave
+        if (!exact || a.segs_per_split * (a.kpr / kBK) % 4 != 0)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL((mxgemm_exact_kernel<64, 64, 1, 1, 4, 1, FA, FB>), dim3(a.total_work), dim3(256), 0,
+                           stream, a);
+        return hipGetLastError();
     default: return hipErrorInvalidValue;
     }
 }

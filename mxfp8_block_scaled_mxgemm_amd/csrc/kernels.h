@@ -16,6 +16,9 @@ struct TileCfg {
     int steps_per_stage;    // K-steps of 128 copied per LDS stage
     bool exact;             // has an exact-mode kernel
     bool automatic;         // the planner may choose it unasked
+    int k_groups;           // groups of waves splitting a work item's K-steps
+                            // (their count must be a multiple of it)
+    bool native;            // has a native-mode kernel
 };
 
 int num_tile_cfgs();

@@ -21,18 +21,22 @@ static const TileCfg kCfgs[] = {
     // 256x256 tile is native only: its exact form's running and fresh FP32
     // accumulators (128 x 128 outputs per wave, twice) would not fit the
     // register file.
-    {256, 256, 512, lds_bytes_for<256, 256, 1>(), 1, 1.00f, 1, false, true},
+    {256, 256, 512, lds_bytes_for<256, 256, 1>(), 1, 1.00f, 1, false, true, 1, true},
     // 256 x 128: exact on eight waves (two 64 x 64 wave tiles per SIMD, so
     // one wave's accumulator flush overlaps the other's MFMAs; measured 248
     // vs 261 us per 2048 x 8192 x 8192 launch with four 128 x 64 waves)
-    {256, 128, 512, lds_bytes_for<256, 128, 1>(), 1, 0.89f, 1, true, true},
-    {128, 128, 256, lds_bytes_for<128, 128, 1>(), 1, 0.53f, 1, true, true},
-    {64, 64, 256, lds_bytes_for<64, 64, 2>(), 2, 0.30f, 2, true, true},
-    {32, 64, 256, lds_bytes_for<32, 64, 3>(), 2, 0.20f, 3, true, true},
-    {16, 64, 256, lds_bytes_for<16, 64, 3>(), 2, 0.12f, 3, true, true},
+    {256, 128, 512, lds_bytes_for<256, 128, 1>(), 1, 0.89f, 1, true, true, 1, true},
+    {128, 128, 256, lds_bytes_for<128, 128, 1>(), 1, 0.53f, 1, true, true, 1, true},
+    {64, 64, 256, lds_bytes_for<64, 64, 2>(), 2, 0.30f, 2, true, true, 1, true},
+    {32, 64, 256, lds_bytes_for<32, 64, 3>(), 2, 0.20f, 3, true, true, 1, true},
+    {16, 64, 256, lds_bytes_for<16, 64, 3>(), 2, 0.12f, 3, true, true, 1, true},
     // one stage holding a work item's whole K range (at most kOneShotSteps);
     // measured slower than the pipelined tiles wherever it fits
-    {32, 64, 256, lds_bytes_for<32, 64, kOneShotSteps>() / 2, 1, 0.20f, kOneShotSteps, true, false},
+    {32, 64, 256, lds_bytes_for<32, 64, kOneShotSteps>() / 2, 1, 0.20f, kOneShotSteps, true, false, 1, true},
+    // exact only: 64 x 64 with four K groups of one 64 x 64 wave each (a
+    // stage holds one K-step per group); measured 52.4 vs 62.8 us per run
+    // of 1024 x 2048 x 4096 (4 ranks) against 64 x 64 tiles with S = 2
+    {64, 64, 256, lds_bytes_for<64, 64, 4>(), 1, 0.60f, 4, true, true, 4, false},
 };
 
 int num_tile_cfgs() { return (int)(sizeof(kCfgs) / sizeof(kCfgs[0])); }

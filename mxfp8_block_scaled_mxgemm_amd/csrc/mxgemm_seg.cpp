@@ -204,6 +204,9 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     if (opts && opts->tile_cfg >= 0 && exact && !mxg::tile_cfg(opts->tile_cfg).exact)
         return fail(MXGEMM_EINVAL, "tile_cfg %d (%d x %d) has no exact-mode kernel", opts->tile_cfg,
                     mxg::tile_cfg(opts->tile_cfg).tile_m, mxg::tile_cfg(opts->tile_cfg).tile_n);
+    if (opts && opts->tile_cfg >= 0 && !exact && !mxg::tile_cfg(opts->tile_cfg).native)
+        return fail(MXGEMM_EINVAL, "tile_cfg %d (%d x %d) has no native-mode kernel", opts->tile_cfg,
+                    mxg::tile_cfg(opts->tile_cfg).tile_m, mxg::tile_cfg(opts->tile_cfg).tile_n);
 
     Choice best = {-1, 1, 1e300, 0};
     int best_w = w_cand[0];
@@ -219,7 +222,7 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
         for (int c = 0; c < ncfg; ++c) {
             if (opts && opts->tile_cfg >= 0 && opts->tile_cfg != c)
                 continue;
-            if (exact && !mxg::tile_cfg(c).exact)
+            if (exact ? !mxg::tile_cfg(c).exact : !mxg::tile_cfg(c).native)
                 continue;
             for (int s = 1; s <= R; ++s) {
                 if (R % s != 0)
@@ -228,6 +231,15 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
                     continue;
                 if (c == mxg::kOneShotCfg && (int64_t)(R / s) * (kpr / 128) > mxg::kOneShotSteps)
                     continue;   // a work item's K range must fit the single stage
+                if ((int64_t)(R / s) * (kpr / 128) % mxg::tile_cfg(c).k_groups != 0)
+                    continue;   // K groups take equal shares of the K-steps
+                // Unasked, K groups only with at least 4 K-steps each: fewer
+                // do not pay for the groups' final reduction and the unhidden
+                // first copy (128 x 256 x 512, one K-step per group: 14.4 us
+                // per run against 11.5 us with 16 x 64 tiles)
+                if (mxg::tile_cfg(c).k_groups > 1 && !(opts && opts->tile_cfg == c) &&
+                    (int64_t)(R / s) * (kpr / 128) < 4LL * mxg::tile_cfg(c).k_groups)
+                    continue;
                 // Some tiles only when asked for (the one-shot tile: measured
                 // against the pipelined 16 x 64 tile, two work-groups per CU,
                 // it was slower on every shape it fits -- 64 x 2048 x 7168:
@@ -264,7 +276,8 @@ int make_plan(mxgemm_seg_plan_t* p, int64_t M, int64_t kpr, int32_t R, int64_t N
     }
     if (best.cfg < 0)
         return fail(MXGEMM_EINVAL, "no plan satisfies the options (split must divide rank_size; "
-                                   "tile_cfg %d needs at most %d K-steps of 128 per split)",
+                                   "tile_cfg %d needs at most %d K-steps of 128 per split; a tile "
+                                   "with K groups needs a multiple of their count)",
                     mxg::kOneShotCfg, mxg::kOneShotSteps);
     const int W = best_w;
     p->chunks_per_window = W;

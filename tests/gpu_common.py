@@ -14,6 +14,28 @@ ATOL = 1e-2
 RTOL = 8e-3
 
 
+# The tile table as the tests see it (index = tile_cfg option).
+NUM_TILE_CFGS = 8
+NATIVE_ONLY_CFG = 0          # 256 x 256: no exact-mode kernel
+ONE_SHOT_CFG, ONE_SHOT_STEPS = 6, 8
+K_GROUP_CFG, K_GROUPS = 7, 4  # 64 x 64 in four K groups: exact only
+
+
+def forced_tile_refused(cfg, split, R, kpr, precision):
+    """True where forcing (cfg, split) must fail with MxgemmError: a
+    one-shot work item longer than its single stage, a tile without a kernel
+    for the precision mode, or K groups that cannot share the work item's
+    K-steps evenly."""
+    steps = (R // split) * (kpr // 128)
+    if cfg == ONE_SHOT_CFG and steps > ONE_SHOT_STEPS:
+        return True
+    if cfg == NATIVE_ONLY_CFG and precision == "exact":
+        return True
+    if cfg == K_GROUP_CFG and (precision == "native" or steps % K_GROUPS != 0):
+        return True
+    return False
+
+
 def torch_cuda():
     import torch
     if not torch.cuda.is_available():

@@ -278,3 +278,32 @@ def test_exact_mode_has_no_256x256_tile():
     assert ei.value.code == pkg._lib.MXGEMM_EINVAL
     p = pkg.plan(8192, 1024, 8, 8192, 512, 4, opts=pkg.options(tile_cfg=0, precision=pkg.PRECISION_NATIVE))
     assert p.tile_cfg == 0
+
+
+def test_k_group_tile_rules():
+    """Configuration 7 (64 x 64 in four K groups) is exact only, and its
+    groups take equal shares of a work item's K-steps: (R / split) *
+    kPerRank / 128 must be a multiple of 4.  The planner never takes it
+    where either fails; forcing it there is an argument error."""
+    # 1024 x 4096 x 2048, 4 ranks: 8 K-steps per rank
+    ok = pkg.plan(1024, 1024, 4, 2048, 256, 2, opts=pkg.options(tile_cfg=7, split=2))
+    assert (ok.tile_cfg, ok.tile_m, ok.tile_n, ok.split) == (7, 64, 64, 2)
+    for bad in (pkg.options(tile_cfg=7, precision=pkg.PRECISION_NATIVE),
+                pkg.options(tile_cfg=7, split=2, precision=pkg.PRECISION_NATIVE)):
+        with pytest.raises(pkg.MxgemmError) as ei:
+            pkg.plan(1024, 1024, 4, 2048, 256, 2, opts=bad)
+        assert ei.value.code == pkg._lib.MXGEMM_EINVAL
+    # kPerRank 256 (2 K-steps per rank), 6 ranks: splits 2 and 6 leave 6 and 2
+    with pytest.raises(pkg.MxgemmError):
+        pkg.plan(120, 256, 6, 200, 24, 4, opts=pkg.options(tile_cfg=7, split=2))
+    assert pkg.plan(120, 256, 6, 200, 24, 4, opts=pkg.options(tile_cfg=7, split=3)).split == 3
+    # without a forced split the planner takes one that fits
+    p = pkg.plan(120, 256, 6, 200, 24, 4, opts=pkg.options(tile_cfg=7))
+    assert ((6 // p.split) * 2) % 4 == 0
+    for w in inputs.WORKLOADS.values():
+        p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf,
+                     opts=pkg.options(precision=pkg.PRECISION_NATIVE))
+        assert p.tile_cfg != 7, w.describe()
+        p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
+        if p.tile_cfg == 7:
+            assert ((w.R // p.split) * (w.kPerRank // 128)) % 4 == 0, w.describe()

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from mxfp8_block_scaled_mxgemm_amd import inputs
-from gpu_common import (report_misses, Case, custom_case, sample_entries, say, summary,
+from gpu_common import (NUM_TILE_CFGS, forced_tile_refused, report_misses, Case, custom_case, sample_entries, say, summary,
                         tail_and_random_entries, torch_cuda, within_tol, workload_case)
 
 pytestmark = pytest.mark.gpu
@@ -110,12 +110,9 @@ def test_parity_outlier_formats_near_zero_and_random(fa, fb):
     assert not bad.any()
 
 
-ONE_SHOT_CFG, ONE_SHOT_STEPS = 6, 8
-
-
 @pytest.mark.parametrize("precision", ["exact", "native"])
 @pytest.mark.parametrize("split", [1, 3])
-@pytest.mark.parametrize("cfg", range(7))
+@pytest.mark.parametrize("cfg", range(NUM_TILE_CFGS))
 @pytest.mark.parametrize("fa,fb", PAIRS, ids=PAIR_IDS)
 def test_parity_forced_tiles_formats(fa, fb, cfg, split, precision):
     """Every tile configuration, split 1 and 3, on the ragged shape (24 rows
@@ -132,8 +129,7 @@ def test_parity_forced_tiles_formats(fa, fb, cfg, split, precision):
     say(f"[parity-fmt-forced] fa={fa} fb={fb} cfg={cfg} split={split} {precision}")
     opts = _opts(precision)
     opts.tile_cfg, opts.split = cfg, split
-    if (cfg == ONE_SHOT_CFG and (6 // split) * (256 // 128) > ONE_SHOT_STEPS) or \
-            (cfg == 0 and precision == "exact"):       # 256 x 256 is native only
+    if forced_tile_refused(cfg, split, 6, 256, precision):
         with pytest.raises(pkg.MxgemmError):
             case.run_gpu(opts=opts)
         return

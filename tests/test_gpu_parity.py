@@ -8,7 +8,8 @@ import pytest
 
 import oracle
 from mxfp8_block_scaled_mxgemm_amd import inputs
-from gpu_common import (report_misses, custom_case, sample_entries, say, summary, tail_and_random_entries,
+from gpu_common import (NATIVE_ONLY_CFG, NUM_TILE_CFGS, forced_tile_refused, report_misses, custom_case,
+                        sample_entries, say, summary, tail_and_random_entries,
                         torch_cuda, within_tol, workload_case)
 
 pytestmark = pytest.mark.gpu
@@ -236,17 +237,13 @@ def test_small_products_next_to_large_ones(precision):
         assert np.all(got == 16.0)
 
 
-ONE_SHOT_CFG, ONE_SHOT_STEPS = 6, 8
-NATIVE_ONLY_CFG = 0        # 256 x 256: no exact-mode kernel
-
-
 @pytest.mark.parametrize("precision", ["exact", "native"])
-@pytest.mark.parametrize("cfg", range(7))
+@pytest.mark.parametrize("cfg", range(NUM_TILE_CFGS))
 @pytest.mark.parametrize("split", [1, 2, 3, 6])
 def test_parity_forced_tiles_ragged(cfg, split, precision):
     """Every tile configuration and split on a ragged shape: window rows
-    (24 per chunk) and N = 200 are not multiples of any tile.  The one-shot
-    configuration takes only splits whose K range fits its single stage."""
+    (24 per chunk) and N = 200 are not multiples of any tile.  Combinations
+    the library must refuse (forced_tile_refused) raise MxgemmError."""
     torch_cuda()
     import mxfp8_block_scaled_mxgemm_amd as pkg
     key = "ragged"
@@ -257,8 +254,7 @@ def test_parity_forced_tiles_ragged(cfg, split, precision):
     say(f"[parity-forced] cfg={cfg} split={split} {precision}")
     prec = pkg.PRECISION_EXACT if precision == "exact" else pkg.PRECISION_NATIVE
     opts = pkg.options(tile_cfg=cfg, split=split, precision=prec)
-    if (cfg == ONE_SHOT_CFG and (6 // split) * (256 // 128) > ONE_SHOT_STEPS) or \
-            (cfg == NATIVE_ONLY_CFG and precision == "exact"):
+    if forced_tile_refused(cfg, split, 6, 256, precision):
         with pytest.raises(pkg.MxgemmError):
             case.run_gpu(opts=opts)
         return
@@ -289,7 +285,7 @@ def test_parity_chunk_tail(shape, precision):
     assert not bad.any()
 
 
-@pytest.mark.parametrize("cfg", range(7))
+@pytest.mark.parametrize("cfg", range(NUM_TILE_CFGS))
 def test_parity_chunk_tail_forced_tiles(cfg):
     """Every tile configuration on a shape whose last chunk is short."""
     torch_cuda()

@@ -3,9 +3,10 @@ GPU), from one parallel compile of every source to assembly:
 - memory is written only through vector instructions: no scalar-cache
   store, atomic, write-back or discard appears anywhere;
 - no kernel spills registers to scratch (and the GEMM kernels spill none
-  at all), and the exact GEMM kernels (256 x 128 on eight waves and
-  128 x 128 on four, with fresh and running FP32 accumulators) fit a CU at
-  one work-group; no 256 x 256 exact kernel is built.
+  at all), and the exact GEMM kernels (256 x 128 on eight waves, 128 x 128
+  on four and 64 x 64 in four K groups, with fresh and running FP32
+  accumulators) fit a CU at one work-group; no 256 x 256 exact kernel is
+  built.
 This file is CPU-only and is not sent to GPU runs."""
 import os
 import re
@@ -79,10 +80,12 @@ def test_no_register_spills(compiled, src):
 
 def test_exact_kernels_fit_one_work_group_per_cu(compiled):
     """256 x 128 runs eight waves (two per SIMD), 128 x 128 four (one per
-    SIMD); either way one work-group fills a CU's LDS share and SIMDs."""
+    SIMD), 64 x 64 four K groups of one wave (one per SIMD); either way one
+    work-group fills a CU's LDS share and SIMDs."""
     _, kernels = compiled["gemm_e4m3_e4m3.hip"]
     assert not [k for k in kernels if "mxgemm_exact_kernelILi256ELi256E" in k]
-    for tile, waves_per_simd in (("ILi256ELi128ELi4ELi2E", 2), ("ILi128ELi128ELi2ELi2E", 1)):
+    for tile, waves_per_simd in (("ILi256ELi128ELi4ELi2ELi1E", 2), ("ILi128ELi128ELi2ELi2ELi1E", 1),
+                                 ("ILi64ELi64ELi1ELi1ELi4E", 1)):
         exact = [v for k, v in kernels.items() if "mxgemm_exact_kernel" + tile in k]
         assert len(exact) == 1, tile
         assert exact[0]["LDS Size"] <= 160 * 1024 and exact[0]["Occupancy"] == waves_per_simd, exact[0]
