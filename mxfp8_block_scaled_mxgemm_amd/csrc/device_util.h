@@ -102,6 +102,36 @@ __device__ __forceinline__ void dma4(const void* g, void* lds)
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 
+// The same copies, from a wave-uniform base plus a 32-bit per-lane byte
+// offset, issued as inline assembly (global_load_lds_dwordx4 / _dword with
+// the SGPR-base address form).  Once the compiler has issued an LDS DMA
+// itself, every later wait for an LDS read becomes lgkmcnt(0): it waits for
+// all reads in flight, including those issued sub-steps ahead, which undoes
+// the GEMM kernels' read-ahead (measured: 225 vs 231 us per 2048 x 8192 x
+// 8192 exact launch, 103 vs 106 us per 2048 x 4096 x 7168 one).  Hidden
+// from the compiler, the copies need explicit ordering, which the GEMM
+// kernels have anyway: a stage is read only after `s_waitcnt vmcnt` and a
+// barrier, and written only after a barrier that ends its reads.  The
+// instruction has no result registers (it writes LDS), and its address
+// registers are read at issue, as for the compiler's own loads.  M0 (the
+// LDS destination) is set by the compiler through the "{m0}" operand; the
+// s_nop gives the wait states an M0 or SGPR write needs before a vector
+// memory instruction reads it.  Extra loads the compiler does not know of
+// only make its own vmcnt waits stricter, never shorter (vector memory
+// loads return in order).
+__device__ __forceinline__ uint32_t lds_addr(void* lds)
+{
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+}
+__device__ __forceinline__ void dma16_at(const void* base, uint32_t off, void* lds)
+{
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds)));
+}
+__device__ __forceinline__ void dma4_at(const void* base, uint32_t off, void* lds)
+{
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base), "{m0}"(lds_addr(lds)));
+}
+
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 // ---- data one work-group writes for another in the same launch ----------

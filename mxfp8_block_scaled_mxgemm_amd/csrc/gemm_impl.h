@@ -132,33 +132,33 @@ __device__ __forceinline__ void copy_issue(const CopyOffsets<BM, BN, NW, MW>& o,
     for (int j = 0; j < G::JA; ++j)
         if (j % nparts == part) {
             if (G::IA % NW == 0 || wave + j * NW < G::IA)
-                dma16(src.a + o.a[j], dst + (wave + j * NW) * 1024);
+                dma16_at(src.a, o.a[j], dst + (wave + j * NW) * 1024);
             else if (pad)
-                dma4(src.as + o.as[0], pad);
+                dma4_at(src.as, o.as[0], pad);
         }
 #pragma unroll
     for (int j = 0; j < G::JB; ++j)
         if (j % nparts == part) {
             if (G::IB % NW == 0 || wave + j * NW < G::IB)
-                dma16(src.b + o.b[j], dst + G::A_BYTES + (wave + j * NW) * 1024);
+                dma16_at(src.b, o.b[j], dst + G::A_BYTES + (wave + j * NW) * 1024);
             else if (pad)
-                dma4(src.as + o.as[0], pad);
+                dma4_at(src.as, o.as[0], pad);
         }
 #pragma unroll
     for (int j = 0; j < G::KSA; ++j)
         if (j % nparts == part) {
             if (G::ISA % NW == 0 || wave + j * NW < G::ISA)
-                dma4(src.as + o.as[j], dst + G::SA_OFF + (wave + j * NW) * 256);
+                dma4_at(src.as, o.as[j], dst + G::SA_OFF + (wave + j * NW) * 256);
             else if (pad)
-                dma4(src.as + o.as[0], pad);
+                dma4_at(src.as, o.as[0], pad);
         }
 #pragma unroll
     for (int j = 0; j < G::KSB; ++j)
         if ((j + 1) % nparts == part) {
             if (G::ISB % NW == 0 || wave + j * NW < G::ISB)
-                dma4(src.bs + o.bs[j], dst + G::SB_OFF + (wave + j * NW) * 256);
+                dma4_at(src.bs, o.bs[j], dst + G::SB_OFF + (wave + j * NW) * 256);
             else if (pad)
-                dma4(src.as + o.as[0], pad);
+                dma4_at(src.as, o.as[0], pad);
         }
 }
 
@@ -631,19 +631,19 @@ __device__ __forceinline__ void copy_one(const CopyOffsets<BM, BN, NW, MW>& o, c
 #pragma unroll
     for (int j = 0; j < G::JA; ++j)
         if (j % nparts == part && n++ == t && (G::IA % NW == 0 || wave + j * NW < G::IA))
-            dma16(src.a + o.a[j], dst + (wave + j * NW) * 1024);
+            dma16_at(src.a, o.a[j], dst + (wave + j * NW) * 1024);
 #pragma unroll
     for (int j = 0; j < G::JB; ++j)
         if (j % nparts == part && n++ == t && (G::IB % NW == 0 || wave + j * NW < G::IB))
-            dma16(src.b + o.b[j], dst + G::A_BYTES + (wave + j * NW) * 1024);
+            dma16_at(src.b, o.b[j], dst + G::A_BYTES + (wave + j * NW) * 1024);
 #pragma unroll
     for (int j = 0; j < G::KSA; ++j)
         if (j % nparts == part && n++ == t && (G::ISA % NW == 0 || wave + j * NW < G::ISA))
-            dma4(src.as + o.as[j], dst + G::SA_OFF + (wave + j * NW) * 256);
+            dma4_at(src.as, o.as[j], dst + G::SA_OFF + (wave + j * NW) * 256);
 #pragma unroll
     for (int j = 0; j < G::KSB; ++j)
         if ((j + 1) % nparts == part && n++ == t && (G::ISB % NW == 0 || wave + j * NW < G::ISB))
-            dma4(src.bs + o.bs[j], dst + G::SB_OFF + (wave + j * NW) * 256);
+            dma4_at(src.bs, o.bs[j], dst + G::SB_OFF + (wave + j * NW) * 256);
 }
 
 template <int BM, int BN, int NW>
