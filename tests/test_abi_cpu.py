@@ -182,9 +182,11 @@ def test_schedule_bijection_on_workloads(name):
         _check_bijection(p, last)
 
 
-@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 7])
 @pytest.mark.parametrize("split", [1, 2, 3])
 def test_schedule_bijection_forced(cfg, split):
+    if cfg == 7 and split == 2:
+        pytest.skip("6 K-steps per work item: not a multiple of the four K groups")
     p = pkg.plan(120, 256, 6, 200, 24, 4, num_cus=16,
                  opts=pkg.options(tile_cfg=cfg, split=split,
                                   precision=pkg.PRECISION_NATIVE if cfg == 0 else -1))
