@@ -676,7 +676,7 @@ __host__ __device__ constexpr int copies_in_part(int part, int nparts)
 // of one pair plus one per pair.  The totals double the accumulator
 // registers, which limits a wave to 128 x 64 outputs.
 //
-// One wave per SIMD, WGM x WGN waves of (BM / WGM) x (BN / WGN); large wave
+// WGM x WGN waves of (BM / WGM) x (BN / WGN), OCC per SIMD; large wave
 // tiles keep the conversion work per MFMA low (each code a wave reads feeds
 // BN / WGN resp. BM / WGM outputs).  A K-step (128 K) is four sub-steps of
 // one MX block (32 K).  Lane group h = lane / 32 takes K [32j + 16h + 8m,
@@ -978,7 +978,7 @@ static hipError_t launch_cfg(const GemmArgs& a, bool exact, hipStream_t stream)
 }
 
 // Large tiles: native on the scaled MFMA kernel (NWM x NWN waves), exact on
-// the pipelined bf16 kernel (EWM x EWN waves, one per SIMD).
+// the pipelined bf16 kernel (EWM x EWN waves, EWM * EWN / 4 per SIMD).
 template <int BM, int BN, int NWM, int NWN, int NOCC, int EWM, int EWN, int FA, int FB>
 static hipError_t launch_large(const GemmArgs& a, bool exact, hipStream_t stream)
 {

@@ -94,7 +94,11 @@ bool fused_combine(int tile_m, int tile_n, int split)
 // work item is bound either by its MFMAs (at the tile's efficiency, shared
 // with the other resident work-groups of the CU) or by the round trips of
 // its copy stages: a stage's copies are waited for before its K-steps
-// start, and a round trip under load takes ~2 us.
+// start, and a round trip under load takes ~2 us.  The constants (the 1.6
+// factor, 4400 clocks per copy round trip, 3000 per work item, 9000 per
+// fused combine) were fitted on MI355X parts that ran these kernels at
+// 1.84-2.2 GHz shader clock under load; the estimate ranks plans and does
+// not predict times, and its units stay 2.4 GHz clocks whatever the clock.
 double estimate(const mxg::TileCfg& t, int64_t rows, int64_t N, int64_t K, int split,
                 int num_cus, bool exact)
 {
