@@ -20,7 +20,8 @@ Prints ONE JSON line (rank 0 / the only rank):
                around each launch, on its stream), against the MI355X dense
                MX-FP8 MFMA peak (the metric's peak; the bf16 MFMA peak of the
                exact mode's contraction beside it) or HBM
-  configs    = the same figures, stream timer only, for the other workloads
+  configs    = the same figures for the other workloads (stream timer, and
+               the mean over replays of a HIP graph of the step beside it)
   measured_peaks = an MFMA-rate probe (scaled FP8 and bf16) and a device copy
                of 1 GiB, the measured denominators beside the published ones
   cpu_baseline = the CPU oracle on a bounded row sample of the headline
@@ -582,6 +583,22 @@ def main():
             torch.cuda.synchronize()
             warm_up(step_c, name)
             cms, _ = timed(step_c, args.config_steps)
+            # the second timer: the step captured once in a HIP graph, replayed
+            gms_graph = None
+            if not args.no_graph:
+                try:
+                    gsc = torch.cuda.Stream()
+                    graph_c = torch.cuda.CUDAGraph()
+                    torch.cuda.synchronize()
+                    with torch.cuda.stream(gsc):
+                        with torch.cuda.graph(graph_c, stream=gsc):
+                            gc.run(aq, as_, bq, bs, cc, stream=gsc)
+                    torch.cuda.synchronize()
+                    warm_up(graph_c.replay, name + " graph")
+                    gms_graph, _ = timed(graph_c.replay, args.config_steps)
+                    del graph_c
+                except Exception as e:  # report the stream timer only
+                    log(f"[bench]   graph capture unavailable ({e})")
             ktc = kernel_times(gc, step_c, 5)
             gms_c = ktc["gemm_ms"] / ktc["gemm_launches"]
             rc = gemm_roofline(wc, pc, gms_c, args.precision, pc["ring"] == pkg.RING_FLAGS)
@@ -591,6 +608,7 @@ def main():
                 "shape": wc.describe(),
                 "ms_per_step_mean": round(mean, 5), "ms_per_step_median": round(med, 5),
                 "ms_per_step_min": round(min(cms), 5),
+                "graph_ms_per_step_mean": round(statistics.mean(gms_graph), 5) if gms_graph else None,
                 "tflops": round(wc.flops / (mean * 1e-3) / 1e12, 3),
                 "pct_of_mxfp8_peak": round(100.0 * wc.flops / (mean * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 2),
                 "hbm_frac_end_to_end": round(wc.algorithmic_bytes / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
@@ -602,8 +620,9 @@ def main():
                 "plan": {k: pc[k] for k in ("tile_m", "tile_n", "split", "chunks_per_window",
                                             "windows", "grid", "ring")},
             }
-            log(f"[bench]   mean {mean:.4f} ms, gemm {rc['gemm_us_per_launch']:.2f} us/launch, "
-                f"roofline {rc['bound']} {rc['frac']:.3f}")
+            log(f"[bench]   mean {mean:.4f} ms"
+                + (f" (graph replays {statistics.mean(gms_graph):.4f} ms)" if gms_graph else "")
+                + f", gemm {rc['gemm_us_per_launch']:.2f} us/launch, roofline {rc['bound']} {rc['frac']:.3f}")
             gc.close()
             del aq, as_, bq, bs, cc
             torch.cuda.empty_cache()
