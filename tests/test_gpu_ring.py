@@ -26,8 +26,10 @@ def test_repeated_runs_identical_and_correct():
     case = _case()
     w = case.w
     ref = case.oracle_full()
-    for opts in (None, pkg.options(split=4, tile_cfg=3)):
-        say(f"[repeat] opts={'auto' if opts is None else 'split4'}")
+    for label, opts in (("auto", None), ("64x64 split 4", pkg.options(split=4, tile_cfg=3)),
+                        ("256x128", pkg.options(split=1, tile_cfg=1)),
+                        ("64x64 K groups", pkg.options(split=1, tile_cfg=7))):
+        say(f"[repeat] opts={label}")
         outs = []
         with pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts) as g:
             for _ in range(5):
@@ -42,14 +44,16 @@ def test_repeated_runs_identical_and_correct():
             assert np.array_equal(o.float().cpu().numpy(), first)   # deterministic
 
 
-def test_graph_capture_replays():
+@pytest.mark.parametrize("tiles", ["auto split 2", "256x128", "64x64 K groups"])
+def test_graph_capture_replays(tiles):
     torch = torch_cuda()
     import mxfp8_block_scaled_mxgemm_amd as pkg
     case = _case()
     w = case.w
-    say("[graph] capture + 4 replays")
-    with pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf,
-                     opts=pkg.options(split=2)) as g:
+    opts = {"auto split 2": pkg.options(split=2), "256x128": pkg.options(split=1, tile_cfg=1),
+            "64x64 K groups": pkg.options(split=1, tile_cfg=7)}[tiles]
+    say(f"[graph] {tiles}: capture + 4 replays")
+    with pkg.SegGemm(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=opts) as g:
         eager = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
         g.run(case.a_q, case.a_s, case.b_q, case.b_s, eager)
         torch.cuda.synchronize()
