@@ -53,25 +53,26 @@ typedef struct mxgemm_seg* mxgemm_seg_t;
  *    is formed exactly (codes are converted to bfloat16 with the block scale
  *    folded in, which is exact for scale bytes >= 3 with E4M3 codes, >= 10
  *    with E5M2) and the products are summed on the bfloat16 MFMA
- *    (v_mfma_f32_32x32x16_bf16 on the 256 x 128 and 128 x 128 tiles,
- *    v_mfma_f32_16x16x32_bf16 on the smaller ones), which adds them into
- *    FP32 in groups of eight.  Each pair of K-steps (256 K) is summed in
- *    fresh accumulators and then added to FP32 running totals, so a large
- *    product rounds the small ones after it only until the pair ends.  The
- *    result is an FP32 sum in a fixed order, rounded once to bfloat16; like
- *    any FP32 sum it can lose small terms to cancellation of large ones
- *    (2^30 + 1 - 2^30 gives 0).  Tested: |C - exact| <= 1e-2 + 8e-3 |exact|
- *    on every output of four measured workloads and, on the 8192-cube
- *    outlier workload, on every output whose |C| is under 5% of the RMS
- *    plus 2^20 random ones; bit-exact results on integer-valued data whose
- *    sums stay below 2^8.  The 256 x 256 tile has no exact-mode kernel.
+ *    (v_mfma_f32_32x32x16_bf16 on the 256 x 128, 128 x 128 and K-group
+ *    64 x 64 tiles, v_mfma_f32_16x16x32_bf16 on the other small ones), which
+ *    adds them into FP32 in groups of eight.  Each pair of K-steps (256 K)
+ *    is summed in fresh accumulators and then added to FP32 running totals,
+ *    so a large product rounds the small ones after it only until the pair
+ *    ends.  The result is an FP32 sum in a fixed order, rounded once to
+ *    bfloat16; like any FP32 sum it can lose small terms to cancellation of
+ *    large ones (2^30 + 1 - 2^30 gives 0).  Tested: |C - exact| <= 1e-2 +
+ *    8e-3 |exact| on every output of the five measured workloads without
+ *    outliers and, on the 8192-cube outlier workload, on every output whose
+ *    |C| is under 5% of the RMS plus 2^20 random ones; bit-exact results on
+ *    integer-valued data whose sums stay below 2^8.  The 256 x 256 tile has
+ *    no exact-mode kernel.
  *  MXGEMM_PRECISION_NATIVE: the CDNA4 block-scaled FP8 MFMA
  *    (v_mfma_scale_f32_32x32x64_f8f6f4 on the large tiles,
  *    v_mfma_scale_f32_16x16x128_f8f6f4 on the small ones) at twice the peak
  *    rate.  Its internal block dot drops products that are ~2^13 times
  *    smaller than another product of the same group of eight, so data with
  *    large in-block dynamic range (outliers) can miss the tolerance above
- *    where C is small; it meets it on the four workloads without outliers. */
+ *    where C is small; it meets it on the five workloads without outliers. */
 enum { MXGEMM_PRECISION_EXACT = 0, MXGEMM_PRECISION_NATIVE = 1 };
 
 /* FP8 formats of the A and B codes.  The pages ship four entries of the
