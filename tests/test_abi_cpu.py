@@ -309,3 +309,29 @@ def test_k_group_tile_rules():
         p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
         if p.tile_cfg == 7:
             assert ((w.R // p.split) * (w.kPerRank // 128)) % 4 == 0, w.describe()
+
+
+def test_plans_on_random_shapes_are_consistent():
+    """For 300 seeded random shapes, both precision modes: the plan's tile
+    has a kernel for the mode, its split divides R, its K groups share the
+    work item's K-steps evenly, the window divides the ring, the windows
+    cover every chunk, the tiles cover the window, and the work items are
+    exactly tiles x splits."""
+    from random_shapes import random_shapes
+    for (R, M, kpr, N, cms, nbuf) in random_shapes(2024, 300):
+        for prec in (pkg.PRECISION_EXACT, pkg.PRECISION_NATIVE):
+            p = pkg.plan(M, kpr, R, N, cms, nbuf, opts=pkg.options(precision=prec))
+            where = (R, M, kpr, N, cms, nbuf, prec)
+            assert p.chunks == -(-M // cms), where
+            assert nbuf % p.chunks_per_window == 0 and p.window_slots * p.chunks_per_window == nbuf, where
+            assert p.windows == -(-p.chunks // p.chunks_per_window), where
+            if p.ring == pkg.RING_EVENTS:
+                assert R % p.split == 0, where
+                steps = (R // p.split) * (kpr // 128)
+                assert p.tile_cfg != 6 or steps <= 8, where
+                assert p.tile_cfg != 7 or (steps % 4 == 0 and prec == pkg.PRECISION_EXACT), where
+                assert not (p.tile_cfg == 0 and prec == pkg.PRECISION_EXACT), where
+                rows = p.chunks_per_window * cms
+                assert p.tiles_m * p.tile_m >= rows and (p.tiles_m - 1) * p.tile_m < rows, where
+                assert p.tiles_n * p.tile_n >= N and (p.tiles_n - 1) * p.tile_n < N, where
+                assert p.work_items == p.tiles_m * p.tiles_n * p.split == p.grid, where
