@@ -100,6 +100,27 @@ def test_e4m3_encode_matches_torch_random():
     assert np.array_equal(ours, ref)
 
 
+def _exhaustive_encode_check(encode, torch_dtype, limit_bits, chunk=1 << 26):
+    """Every fp32 bit pattern with |v| <= the format's largest finite value
+    (both signs), in chunks: the oracle's encoder against torch's cast."""
+    for sign in (0, 0x80000000):
+        for lo in range(0, limit_bits + 1, chunk):
+            hi = min(lo + chunk, limit_bits + 1)
+            bits = np.arange(lo, hi, dtype=np.uint32) | np.uint32(sign)
+            f = bits.view(np.float32)
+            ref = torch.from_numpy(f).to(torch_dtype).view(torch.uint8).numpy()
+            ours = encode(f.astype(np.float64))
+            if not np.array_equal(ours, ref):
+                i = int(np.nonzero(ours != ref)[0][0])
+                raise AssertionError(f"{float(f[i])!r} (bits {int(bits[i]):#010x}): oracle {int(ours[i]):#04x}, "
+                                     f"torch {int(ref[i]):#04x}")
+
+
+def test_e4m3_encode_exhaustive_matches_torch():
+    """All 2 x 1.14e9 fp32 values with |v| <= 448 (0x43E00000)."""
+    _exhaustive_encode_check(oracle.e4m3_encode, torch.float8_e4m3fn, 0x43E00000)
+
+
 def test_e4m3_encode_decode_roundtrip_all_finite_codes():
     codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
     vals = oracle.e4m3_value(codes)

@@ -88,6 +88,22 @@ def test_e5m2_encode_matches_torch_random():
     assert np.array_equal(oracle.e5m2_encode(f.astype(np.float64)), _torch_e5m2_encode(f))
 
 
+def test_e5m2_encode_exhaustive_matches_torch():
+    """All 2 x 1.19e9 fp32 values with |v| <= 57344 (0x47600000), in
+    chunks, against torch's cast."""
+    chunk = 1 << 26
+    for sign in (0, 0x80000000):
+        for lo in range(0, 0x47600000 + 1, chunk):
+            hi = min(lo + chunk, 0x47600000 + 1)
+            bits = np.arange(lo, hi, dtype=np.uint32) | np.uint32(sign)
+            f = bits.view(np.float32)
+            ref = torch.from_numpy(f).to(torch.float8_e5m2).view(torch.uint8).numpy()
+            ours = oracle.e5m2_encode(f.astype(np.float64))
+            if not np.array_equal(ours, ref):
+                i = int(np.nonzero(ours != ref)[0][0])
+                raise AssertionError(f"{float(f[i])!r}: oracle {int(ours[i]):#04x}, torch {int(ref[i]):#04x}")
+
+
 def test_e5m2_encode_saturates_and_keeps_nan():
     big = np.array([57344.0, 61439.99, 61440.0, 1e6, math.inf, -61440.0, -math.inf])
     assert oracle.e5m2_encode(big).tolist() == [0x7B, 0x7B, 0x7B, 0x7B, 0x7B, 0xFB, 0xFB]
