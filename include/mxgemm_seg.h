@@ -153,8 +153,8 @@ typedef struct mxgemm_seg_plan {
  *   6   32 x  64, one stage holding a work item's whole K range, at most 8
  *       steps ((rank_size / split) * kPerRank / 128 <= 8); planned only when
  *       asked for
- *   7   64 x  64, exact only: four waves of 64 x 64, each taking every
- *       fourth K-step of the work item, their sums added at the end; needs
+ *   7   64 x  64: four waves of 64 x 64, each taking every fourth K-step
+ *       of the work item, their sums added at the end; needs
  *       (rank_size / split) * kPerRank / 128 to be a multiple of 4
  * The planner picks the tile, split and window by a cost model; forcing a
  * value the problem cannot take fails with MXGEMM_EINVAL. */

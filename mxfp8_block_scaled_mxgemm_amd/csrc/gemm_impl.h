@@ -289,6 +289,49 @@ __device__ __forceinline__ void store_tile_lds(const GemmArgs& p, v16f (&acc)[GA
     }
 }
 
+// K groups (WGK groups of NWG waves sharing one tile, each summing its own
+// share of the K-steps into v16f accumulators of GA x GB 32 x 32 blocks):
+// groups 1 .. WGK - 1 leave their sums in `red` (elements 4q .. 4q + 3 of
+// block b of a lane as one 16-byte piece at float (b * 4 + q) * 256 + 4 *
+// lane of the wave's slot of GA * GB * 1024 floats), and group 0 adds them
+// in group order.  Every thread of the work-group calls it: the first
+// barrier ends the K loop's LDS reads, the second publishes the sums.
+template <int NWG, int WGK, int GA, int GB>
+__device__ __forceinline__ void reduce_k_groups(v16f (&acc)[GA][GB], float* red, int wk, int wl, int lane)
+{
+    constexpr int SLOT = GA * GB * 1024;
+    __syncthreads();
+    if (wk > 0) {
+        float* slot = red + ((wk - 1) * NWG + wl) * SLOT;
+#pragma unroll
+        for (int i = 0; i < GA; ++i)
+#pragma unroll
+            for (int g = 0; g < GB; ++g)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4f*>(slot + ((i * GB + g) * 4 + q) * 256 + 4 * lane) =
+                        v4f{acc[i][g][4 * q], acc[i][g][4 * q + 1], acc[i][g][4 * q + 2], acc[i][g][4 * q + 3]};
+    }
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll 1
+        for (int k = 1; k < WGK; ++k) {
+            const float* slot = red + ((k - 1) * NWG + wl) * SLOT;
+#pragma unroll
+            for (int i = 0; i < GA; ++i)
+#pragma unroll
+                for (int g = 0; g < GB; ++g)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v4f x = *reinterpret_cast<const v4f*>(slot + ((i * GB + g) * 4 + q) * 256 + 4 * lane);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[i][g][4 * q + e] += x[e];
+                    }
+        }
+    }
+}
+
 // Split-K, fused combine: once this work-group's partials are stored
 // (device-scope), count its arrival at the tile; the last split to arrive
 // sums the tile's partials in split order into C and sets the count back to
@@ -319,12 +362,19 @@ __device__ __forceinline__ void split_combine(const GemmArgs& p, const TileCoord
 // small tiles keep several K-steps' copies in flight (their K loop is bound
 // by copy latency, not by the MFMAs).  ONE: a work item has at most CH
 // K-steps, all copied at once into a single stage (skinny shapes, where the
-// whole K range of a split fits in LDS).
-template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT, int MW, int CH, bool ONE, int FA, int FB>
-__global__ void __launch_bounds__(WGM * WGN * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+// whole K range of a split fits in LDS).  WGK > 1 (native 32-wide form
+// only): K groups as in mxgemm_exact_kernel -- WGK groups of WGM x WGN waves
+// share the tile, group k taking K-steps k, k + WGK, ...; a stage holds one
+// K-step per group, copied by that group; the groups' sums are added in
+// group order at the end.
+template <int BM, int BN, int WGM, int WGN, int OCC, bool EXACT, int MW, int CH, bool ONE, int FA, int FB,
+          int WGK = 1>
+__global__ void __launch_bounds__(WGM * WGN * WGK * 64) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 mxgemm_kernel(GemmArgs p)
 {
-    constexpr int NW = WGM * WGN;
+    static_assert(WGK == 1 || (!EXACT && MW == 32 && CH == 1 && !ONE), "K groups: native 32-wide form, CH = 1");
+    constexpr int NWG = WGM * WGN;          // waves of one K group
+    constexpr int NW = NWG * WGK;
     constexpr int TM = BM / WGM, TN = BN / WGN;
     constexpr int GA = TM / MW, GB = TN / MW;
     static_assert(TM % MW == 0 && TN % MW == 0, "wave tile must be a multiple of the MFMA width");
@@ -332,14 +382,14 @@ mxgemm_kernel(GemmArgs p)
     static_assert(!(EXACT && MW == 32), "the 32-wide exact form is mxgemm_exact_kernel");
     typedef typename AccT<MW>::T acc_t;
     constexpr int NACC = AccT<MW>::N;
-    typedef StageGeom<BM, BN, NW> G;
+    typedef StageGeom<BM, BN, NWG> G;       // one K-step, copied by one K group
 
     // Two distinct LDS objects (not one array indexed by the step parity):
     // the compiler then knows a step's copies into one stage never alias
     // the reads of the other, and does not wait for the copies before the
-    // reads.
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[CH * G::STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[ONE ? 16 : CH * G::STAGE];
+    // reads.  Sub-stage c * WGK + k holds K-step c of the stage for group k.
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[CH * WGK * G::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[ONE ? 16 : CH * WGK * G::STAGE];
     __shared__ __attribute__((aligned(256))) uint8_t pad_lds[ONE ? 256 : 4];
     // copy instructions per wave and K-step when padded (ONE)
     constexpr int kCopiesPerStep = G::JA + G::JB + G::KSA + G::KSB;
@@ -348,7 +398,8 @@ mxgemm_kernel(GemmArgs p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform
-    const int wm = wave / WGN, wn = wave % WGN;
+    const int wk = wave / NWG, wl = wave % NWG;                  // K group, wave in the group
+    const int wm = wl / WGN, wn = wl % WGN;
     const int lr = lane & (MW - 1);         // row / column of the lane in a block
     const int lq = lane / MW;               // lane group
 
@@ -361,10 +412,12 @@ mxgemm_kernel(GemmArgs p)
     {
         const TileCoord tc = decode_work(w, p.tiles_m, p.tiles_n, p.split, p.group_n);
         const int m0 = tc.tm * BM, n0 = tc.tn * BN;
-        CopyOffsets<BM, BN, NW, MW> co;
-        copy_offsets(p, m0, n0, wave, lane, co);
+        CopyOffsets<BM, BN, NWG, MW> co;
+        copy_offsets(p, m0, n0, wl, lane, co);
         const int seg0 = tc.ks * p.segs_per_split;
-        const int nsteps = p.segs_per_split * (p.kpr / kBK);
+        // the group's K-steps: s -> work-item K-step WGK s + wk
+        const int nsteps = p.segs_per_split * (p.kpr / kBK) / WGK;
+        auto src_of = [&](int s) { return step_src(p, seg0, n0, WGK * s + wk); };
 
         acc_t acc[GA][GB];
         // exact mode: running totals; each pair of K-steps is summed in
@@ -385,7 +438,7 @@ mxgemm_kernel(GemmArgs p)
 #pragma unroll
         for (int c = 0; c < CH; ++c)
             if (c < nsteps)
-                copy_issue(co, step_src(p, seg0, n0, c), stage0 + c * G::STAGE, wave, 0, 1,
+                copy_issue(co, src_of(c), stage0 + (c * WGK + wk) * G::STAGE, wl, 0, 1,
                            ONE ? pad_lds : nullptr);
         if (!ONE) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -398,7 +451,7 @@ mxgemm_kernel(GemmArgs p)
 #pragma unroll
             for (int c = 0; c < CH; ++c)
                 if (!ONE && (t + 1) * CH + c < nsteps)
-                    copy_issue(co, step_src(p, seg0, n0, (t + 1) * CH + c), nxt + c * G::STAGE, wave);
+                    copy_issue(co, src_of((t + 1) * CH + c), nxt + (c * WGK + wk) * G::STAGE, wl);
 #pragma unroll
             for (int c = 0; c < CH; ++c) {
             if (t * CH + c >= nsteps)
@@ -410,7 +463,7 @@ mxgemm_kernel(GemmArgs p)
                 wait_steps<kCopiesPerStep, CH - 1>(nsteps - 1 - c);
                 __syncthreads();
             }
-            const uint8_t* sub = cur + c * G::STAGE;
+            const uint8_t* sub = cur + (c * WGK + wk) * G::STAGE;
             // Row r of a fragment group is r = group base + lr with the
             // group base a multiple of MW >= 16, so the swizzle key of r
             // equals that of lr: a lane's swizzled byte offsets differ
@@ -588,24 +641,39 @@ mxgemm_kernel(GemmArgs p)
                 kstage(t + 1, stage1, stage0);
         }
 
+        if constexpr (WGK > 1) {
+            // groups 1 .. WGK - 1 pass their sums through stage 0
+            static_assert((WGK - 1) * NWG * TM * TN * 4 <= WGK * G::STAGE, "sums of the other groups fit a stage");
+            reduce_k_groups<NWG, WGK, GA, GB>(acc, reinterpret_cast<float*>(stage0), wk, wl, lane);
+        }
         if constexpr (!EXACT && MW == 32 && !ONE) {
             // Native large tiles: bfloat16 C as whole rows through LDS, as
             // in the exact kernel (the stages are free: every wave has
-            // passed the last stage's barrier); waves 0 .. NW/2 - 1 use
-            // stage 0, the others stage 1.
-            static_assert(NW % 2 == 0 && (NW / 2) * TM * TN * 2 <= CH * G::STAGE,
-                          "half the wave tiles of bf16 per stage");
+            // passed the last stage's barrier).  One K group: waves 0 ..
+            // NW/2 - 1 use stage 0, the others stage 1; several: group 0
+            // stores through stage 1 (stage 0 holds the other groups' sums).
             if (p.split == 1 && (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && (p.N & 7) == 0) {
-                __syncthreads();
-                uint8_t* buf = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * (TM * TN * 2);
-                store_tile_lds<GA, GB, TM, TN>(p, acc, buf, m0 + wm * TM, n0 + wn * TN, lane);
+                if constexpr (WGK == 1) {
+                    static_assert(NW % 2 == 0 && (NW / 2) * TM * TN * 2 <= CH * G::STAGE,
+                                  "half the wave tiles of bf16 per stage");
+                    __syncthreads();
+                    uint8_t* buf = (wave < NW / 2 ? stage0 : stage1) + (wave % (NW / 2)) * (TM * TN * 2);
+                    store_tile_lds<GA, GB, TM, TN>(p, acc, buf, m0 + wm * TM, n0 + wn * TN, lane);
+                } else {
+                    static_assert(NWG * TM * TN * 2 <= WGK * G::STAGE, "bf16 wave tiles of one group fit a stage");
+                    if (wk == 0)
+                        store_tile_lds<GA, GB, TM, TN>(p, acc, stage1 + wl * (TM * TN * 2), m0 + wm * TM,
+                                                       n0 + wn * TN, lane);
+                }
                 return;
             }
         }
-        if constexpr (EXACT)
-            store_tile<GA, GB, MW>(p, tc, tot, m0 + wm * TM, n0 + wn * TN, lane);
-        else
-            store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
+        if (wk == 0) {
+            if constexpr (EXACT)
+                store_tile<GA, GB, MW>(p, tc, tot, m0 + wm * TM, n0 + wn * TN, lane);
+            else
+                store_tile<GA, GB, MW>(p, tc, acc, m0 + wm * TM, n0 + wn * TN, lane);
+        }
         if (p.split > 1 && p.fused)
             split_combine<BM, BN>(p, tc, m0, n0);
     }
@@ -902,42 +970,9 @@ mxgemm_exact_kernel(GemmArgs p)
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no copy outlives the work-group
 
         if constexpr (WGK > 1) {
-            // Groups 1 .. WGK - 1 leave their totals in stage 0 (elements
-            // 4q .. 4q + 3 of accumulator block b of a lane as one 16-byte
-            // piece at float (b * 4 + q) * 256 + 4 * lane of the wave's
-            // slot), group 0 adds them in group order.
+            // groups 1 .. WGK - 1 pass their totals through stage 0
             static_assert((WGK - 1) * NWG * TM * TN * 4 <= WGK * G::STAGE, "totals of the other groups fit a stage");
-            float* red = reinterpret_cast<float*>(stage0);
-            __syncthreads();                               // every wave has read its last codes
-            if (wk > 0) {
-                float* slot = red + ((wk - 1) * NWG + wl) * (TM * TN);
-#pragma unroll
-                for (int i = 0; i < GA; ++i)
-#pragma unroll
-                    for (int g = 0; g < GB; ++g)
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<v4f*>(slot + ((i * GB + g) * 4 + q) * 256 + 4 * lane) =
-                                v4f{tot[i][g][4 * q], tot[i][g][4 * q + 1], tot[i][g][4 * q + 2], tot[i][g][4 * q + 3]};
-            }
-            __syncthreads();
-            if (wk == 0) {
-#pragma unroll 1
-                for (int k = 1; k < WGK; ++k) {
-                    const float* slot = red + ((k - 1) * NWG + wl) * (TM * TN);
-#pragma unroll
-                    for (int i = 0; i < GA; ++i)
-#pragma unroll
-                        for (int g = 0; g < GB; ++g)
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const v4f x = *reinterpret_cast<const v4f*>(slot + ((i * GB + g) * 4 + q) * 256 + 4 * lane);
-#pragma unroll
-                                for (int e = 0; e < 4; ++e)
-                                    tot[i][g][4 * q + e] += x[e];
-                            }
-                }
-            }
+            reduce_k_groups<NWG, WGK, GA, GB>(tot, reinterpret_cast<float*>(stage0), wk, wl, lane);
         }
         if (p.split == 1 && (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && (p.N & 7) == 0) {
             // bfloat16 C through LDS: both stages are free once every wave
@@ -1014,11 +1049,15 @@ hipError_t launch_gemm_fmt(int cfg, bool exact, const GemmArgs& a, hipStream_t s
     case 5: return launch_cfg<16, 64, 1, 4, 2, 16, 3, false, FA, FB>(a, exact, stream);
     case 6: return launch_cfg<32, 64, 1, 4, 1, 16, kOneShotSteps, true, FA, FB>(a, exact, stream);
     case 7:
-        // exact only: 64 x 64 in four K groups of one 64 x 64 wave
-        if (!exact || a.segs_per_split * (a.kpr / kBK) % 4 != 0)
+        // 64 x 64 in four K groups of one 64 x 64 wave
+        if (a.segs_per_split * (a.kpr / kBK) % 4 != 0)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL((mxgemm_exact_kernel<64, 64, 1, 1, 4, 1, FA, FB>), dim3(a.total_work), dim3(256), 0,
-                           stream, a);
+        if (exact)
+            hipLaunchKernelGGL((mxgemm_exact_kernel<64, 64, 1, 1, 4, 1, FA, FB>), dim3(a.total_work), dim3(256), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((mxgemm_kernel<64, 64, 1, 1, 1, false, 32, 1, false, FA, FB, 4>), dim3(a.total_work),
+                               dim3(256), 0, stream, a);
         return hipGetLastError();
     default: return hipErrorInvalidValue;
     }

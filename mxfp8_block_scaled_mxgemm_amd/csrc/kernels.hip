@@ -33,10 +33,10 @@ static const TileCfg kCfgs[] = {
     // one stage holding a work item's whole K range (at most kOneShotSteps);
     // measured slower than the pipelined tiles wherever it fits
     {32, 64, 256, lds_bytes_for<32, 64, kOneShotSteps>() / 2, 1, 0.20f, kOneShotSteps, true, false, 1, true},
-    // exact only: 64 x 64 with four K groups of one 64 x 64 wave each (a
-    // stage holds one K-step per group); measured 52.4 vs 62.8 us per run
-    // of 1024 x 2048 x 4096 (4 ranks) against 64 x 64 tiles with S = 2
-    {64, 64, 256, lds_bytes_for<64, 64, 4>(), 1, 0.60f, 4, true, true, 4, false},
+    // 64 x 64 with four K groups of one 64 x 64 wave each (a stage holds one
+    // K-step per group); exact mode measured 52.4 vs 62.8 us per run of
+    // 1024 x 2048 x 4096 (4 ranks) against 64 x 64 tiles with S = 2
+    {64, 64, 256, lds_bytes_for<64, 64, 4>(), 1, 0.60f, 4, true, true, 4, true},
 };
 
 int num_tile_cfgs() { return (int)(sizeof(kCfgs) / sizeof(kCfgs[0])); }

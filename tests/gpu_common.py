@@ -18,7 +18,7 @@ RTOL = 8e-3
 NUM_TILE_CFGS = 8
 NATIVE_ONLY_CFG = 0          # 256 x 256: no exact-mode kernel
 ONE_SHOT_CFG, ONE_SHOT_STEPS = 6, 8
-K_GROUP_CFG, K_GROUPS = 7, 4  # 64 x 64 in four K groups: exact only
+K_GROUP_CFG, K_GROUPS = 7, 4  # 64 x 64 in four K groups
 
 
 def forced_tile_refused(cfg, split, R, kpr, precision):
@@ -31,7 +31,7 @@ def forced_tile_refused(cfg, split, R, kpr, precision):
         return True
     if cfg == NATIVE_ONLY_CFG and precision == "exact":
         return True
-    if cfg == K_GROUP_CFG and (precision == "native" or steps % K_GROUPS != 0):
+    if cfg == K_GROUP_CFG and steps % K_GROUPS != 0:
         return True
     return False
 

@@ -283,18 +283,14 @@ def test_exact_mode_has_no_256x256_tile():
 
 
 def test_k_group_tile_rules():
-    """Configuration 7 (64 x 64 in four K groups) is exact only, and its
-    groups take equal shares of a work item's K-steps: (R / split) *
-    kPerRank / 128 must be a multiple of 4.  The planner never takes it
-    where either fails; forcing it there is an argument error."""
+    """Configuration 7 (64 x 64 in four K groups, both modes): its groups
+    take equal shares of a work item's K-steps, so (R / split) * kPerRank /
+    128 must be a multiple of 4.  The planner never takes it where that
+    fails; forcing it there is an argument error."""
     # 1024 x 4096 x 2048, 4 ranks: 8 K-steps per rank
-    ok = pkg.plan(1024, 1024, 4, 2048, 256, 2, opts=pkg.options(tile_cfg=7, split=2))
-    assert (ok.tile_cfg, ok.tile_m, ok.tile_n, ok.split) == (7, 64, 64, 2)
-    for bad in (pkg.options(tile_cfg=7, precision=pkg.PRECISION_NATIVE),
-                pkg.options(tile_cfg=7, split=2, precision=pkg.PRECISION_NATIVE)):
-        with pytest.raises(pkg.MxgemmError) as ei:
-            pkg.plan(1024, 1024, 4, 2048, 256, 2, opts=bad)
-        assert ei.value.code == pkg._lib.MXGEMM_EINVAL
+    for prec in (pkg.PRECISION_EXACT, pkg.PRECISION_NATIVE):
+        ok = pkg.plan(1024, 1024, 4, 2048, 256, 2, opts=pkg.options(tile_cfg=7, split=2, precision=prec))
+        assert (ok.tile_cfg, ok.tile_m, ok.tile_n, ok.split) == (7, 64, 64, 2)
     # kPerRank 256 (2 K-steps per rank), 6 ranks: splits 2 and 6 leave 6 and 2
     with pytest.raises(pkg.MxgemmError):
         pkg.plan(120, 256, 6, 200, 24, 4, opts=pkg.options(tile_cfg=7, split=2))
@@ -303,12 +299,10 @@ def test_k_group_tile_rules():
     p = pkg.plan(120, 256, 6, 200, 24, 4, opts=pkg.options(tile_cfg=7))
     assert ((6 // p.split) * 2) % 4 == 0
     for w in inputs.WORKLOADS.values():
-        p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf,
-                     opts=pkg.options(precision=pkg.PRECISION_NATIVE))
-        assert p.tile_cfg != 7, w.describe()
-        p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf)
-        if p.tile_cfg == 7:
-            assert ((w.R // p.split) * (w.kPerRank // 128)) % 4 == 0, w.describe()
+        for prec in (pkg.PRECISION_EXACT, pkg.PRECISION_NATIVE):
+            p = pkg.plan(w.M, w.kPerRank, w.R, w.N, w.commMSize, w.nbuf, opts=pkg.options(precision=prec))
+            if p.tile_cfg == 7:
+                assert ((w.R // p.split) * (w.kPerRank // 128)) % 4 == 0, w.describe()
 
 
 def test_plans_on_random_shapes_are_consistent():
@@ -329,7 +323,7 @@ def test_plans_on_random_shapes_are_consistent():
                 assert R % p.split == 0, where
                 steps = (R // p.split) * (kpr // 128)
                 assert p.tile_cfg != 6 or steps <= 8, where
-                assert p.tile_cfg != 7 or (steps % 4 == 0 and prec == pkg.PRECISION_EXACT), where
+                assert p.tile_cfg != 7 or steps % 4 == 0, where
                 assert not (p.tile_cfg == 0 and prec == pkg.PRECISION_EXACT), where
                 rows = p.chunks_per_window * cms
                 assert p.tiles_m * p.tile_m >= rows and (p.tiles_m - 1) * p.tile_m < rows, where
